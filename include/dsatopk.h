@@ -1,0 +1,161 @@
+/*
+ * dsatopk.h - C ABI of the dsatopk library: per-row windowed top-k selection
+ * over fp32 indexer scores with a fused RAGGED or PAGED emit, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (DeepSeek-V4 DSA indexer top-k transform, as described in
+ * the sglang PR digests on prhub.com.cn):
+ *
+ *   For each row b, with L = max(seq_lens[b], 0) and s = row_starts[b]
+ *   (0 when row_starts is NULL), select the k largest scores among
+ *   scores[b * score_stride + s + j] for window positions j in [0, L).
+ *   Equal scores (IEEE ==, so -0.0 equals +0.0) are ordered by lower
+ *   position first. Rows with L <= k select every position 0 .. L-1 and do
+ *   not read their scores. Each selected position j is emitted as
+ *     RAGGED: j + out_offsets[b]
+ *     PAGED:  page_table[b * page_table_stride + j / page_size] * page_size
+ *             + j % page_size
+ *   into row b of out ([num_rows, k] int32). The first min(k, L) slots of a
+ *   row hold the selection in an unspecified order; slots min(k, L) .. k-1
+ *   hold -1.
+ *   Sources: PR #35175 digest ("RAGGED prefill top-k moved to the v2 JIT
+ *   kernel"), section "Key source excerpts": topk_ragged_kernel (window,
+ *   trivial path, -1 padding, output = position + out_offsets[b]) and
+ *   TopKProblem (emit adds the bias; transform_output maps through the page
+ *   table with page_bits = log2(page_size)). PR #26788 digest ("faster top-k
+ *   + page-table transform (runtime k <= 2048)"), "Key source excerpts":
+ *   plan_topk_v2 / topk_transform_512_v2 signatures, runtime k.
+ *
+ * Conventions for every call below:
+ *   - Pointers named scores, seq_lens, row_starts, out_offsets, page_table,
+ *     plan and out are DEVICE pointers. `stream` is a hipStream_t (NULL is
+ *     the default stream).
+ *   - Calls are asynchronous on `stream`, allocate nothing, never
+ *     synchronize the host, and only launch kernels (no memset or copy
+ *     nodes), so they may be captured in a HIP graph.
+ *   - The caller owns every buffer. `scores` is only read; it is never
+ *     written, not even outside the window.
+ *   - Host-checkable preconditions are checked before anything is launched;
+ *     on error nothing is written and a status other than DSATOPK_OK is
+ *     returned. No call aborts or throws.
+ *   - The library holds no global state and is safe to call from several
+ *     host threads. Two calls that share one plan buffer must not overlap
+ *     in time (see dsatopk_plan).
+ */
+#ifndef DSATOPK_H_
+#define DSATOPK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    DSATOPK_OK = 0,
+    /* k outside [1, DSATOPK_MAX_K]; num_rows < 0; a required pointer is NULL;
+       score_stride < 1; page_size not a power of two in [1, 2^20];
+       page_table_stride < 1. */
+    DSATOPK_ERR_INVALID_ARG = 1,
+    /* scores not 16-byte aligned, or score_stride not a multiple of 4. */
+    DSATOPK_ERR_ALIGNMENT = 2,
+    /* plan_bytes smaller than dsatopk_plan_bytes(num_rows). */
+    DSATOPK_ERR_PLAN_TOO_SMALL = 3,
+    /* the HIP runtime reported an error (no device, launch failure). */
+    DSATOPK_ERR_HIP = 4
+};
+
+/* Largest k (runtime value; one build serves every k). The pages bound the
+   v2 kernel to 0 < topk <= 2048 (PR #35175 digest, backend dispatch
+   condition; PR #26788 digest title). */
+#define DSATOPK_MAX_K 2048
+
+/* Longest supported window. Longer windows are a device-side precondition
+   violation (see dsatopk_paged). */
+#define DSATOPK_MAX_SEQ_LEN 131072
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dsatopk_status_string(int status);
+
+/* Size in bytes of the plan buffer for `num_rows` rows (0 if num_rows < 0). */
+size_t dsatopk_plan_bytes(int32_t num_rows);
+
+/*
+ * dsatopk_plan - build the device-side schedule for a batch.
+ *
+ * Reads seq_lens[num_rows] (int32, device) and writes the plan buffer
+ * (device, plan_bytes >= dsatopk_plan_bytes(num_rows), 16-byte aligned):
+ * which rows are long enough to be cut into several workgroup segments and
+ * how many, plus the zeroed exchange area those segments synchronise
+ * through. Everything is computed on the device; nothing is read back.
+ *
+ * The plan only schedules: a call given a plan built from different
+ * seq_lens, or no plan at all (NULL), returns the same outputs. A plan
+ * must come from a dsatopk_plan call with the same num_rows and k. A plan
+ * may be reused by any number of later transform calls (one per layer, say)
+ * as long as those calls do not run concurrently: each call leaves the
+ * exchange area zeroed again for the next one.
+ *
+ * Source: PR #26788 digest, "Key source excerpts", plan_topk_v2 (a device
+ * plan built from seq_lens and reused by the transform); the layout here is
+ * this library's own.
+ *
+ * Errors: DSATOPK_ERR_INVALID_ARG (num_rows < 0, k outside [1, 2048],
+ * NULL seq_lens or plan with num_rows > 0), DSATOPK_ERR_PLAN_TOO_SMALL,
+ * DSATOPK_ERR_HIP. num_rows == 0 is a no-op.
+ */
+int dsatopk_plan(const int32_t* seq_lens, int32_t num_rows, int32_t k, void* plan,
+                 size_t plan_bytes, void* stream);
+
+/*
+ * dsatopk_paged - top-k with the PAGED emit.
+ *
+ *   scores            fp32 [num_rows, score_stride], row-major, 16-B aligned
+ *                     base, score_stride % 4 == 0. Read only.
+ *   seq_lens          int32 [num_rows]; negative values are read as 0.
+ *   row_starts        int32 [num_rows] or NULL (every window starts at
+ *                     column 0). Any residue modulo 4 is allowed.
+ *   page_table        int32 [num_rows, page_table_stride]; entry
+ *                     j / page_size of row b is the physical page of window
+ *                     position j.
+ *   page_size         power of two in [1, 2^20].
+ *   num_rows, k       0 <= num_rows; 1 <= k <= 2048.
+ *   plan, plan_bytes  from dsatopk_plan, or NULL / 0.
+ *   out               int32 [num_rows, k], written (all of it).
+ *
+ * Device-side preconditions (not checkable without reading device memory,
+ * so not checked): 0 <= row_starts[b]; row_starts[b] + seq_len_b <=
+ * score_stride; seq_len_b <= 131072; page_table_stride >= ceil(seq_len_b /
+ * page_size); every emitted value < 2^31. NaN scores are outside the
+ * contract (the selection stays inside the window, but which NaNs are
+ * picked is unspecified).
+ *
+ * Errors: DSATOPK_ERR_INVALID_ARG, DSATOPK_ERR_ALIGNMENT,
+ * DSATOPK_ERR_PLAN_TOO_SMALL, DSATOPK_ERR_HIP. num_rows == 0 is a no-op.
+ */
+int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                  const int32_t* row_starts, const int32_t* page_table,
+                  int64_t page_table_stride, int32_t page_size, int32_t num_rows, int32_t k,
+                  void* plan, size_t plan_bytes, int32_t* out, void* stream);
+
+/*
+ * dsatopk_ragged - top-k with the RAGGED emit: out = j + out_offsets[b].
+ *
+ * Arguments as for dsatopk_paged, with out_offsets int32 [num_rows]
+ * (device) in place of the page table. With out_offsets == row_starts the
+ * outputs are absolute columns of the score row (PR #35175 digest,
+ * "Impact": the output is then the token's position in the flattened KV).
+ *
+ * Errors: as dsatopk_paged.
+ */
+int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                   const int32_t* row_starts, const int32_t* out_offsets, int32_t num_rows,
+                   int32_t k, void* plan, size_t plan_bytes, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSATOPK_H_ */
