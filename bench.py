@@ -1,0 +1,249 @@
+"""Benchmark of the dsatopk hot path on one GPU; prints one JSON line.
+
+Step: one pass of the whole path over one batch: dsatopk_plan followed by
+dsatopk_paged on the ``paged_decode`` workload (128 rows x 8192 fp32 scores,
+k = 2048, page size 64, random page tables). Inputs are resident in HBM;
+every step reads a different copy of the scores from a rotation of at least
+1 GiB so that score reads miss the 256 MB Infinity Cache.
+
+Also reported (same JSON line):
+  roofline      the paged transform kernel: algorithmic bytes per launch
+                (scores of rows with L > k, outputs, page-table entries,
+                lengths) over its mean launch time from HIP events.
+  sustained     the same per-row shapes with enough rows for >= 1 GiB of
+                scores per launch (paged_decode x32768, paged_long x2048).
+  workloads     every named workload, one launch per iteration, cold.
+  cpu_baseline  the oracle on this host's cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA top-k rows/s + achieved HBM GB/s (paged decode, L=8K–128K, k=2048)"
+HBM_PEAK_GBPS = 8000.0
+ROTATION_BYTES = 1 << 30
+
+
+def algorithmic_bytes(p) -> dict:
+    """Bytes one launch must move: scores of rows with L > k, the k int32
+    outputs of every row, the page-table entries of selected rows' windows,
+    and the per-row metadata (length, start, offset)."""
+    L = p.window_lengths()
+    score = int(4 * L[L > p.k].sum())
+    out = 4 * p.k * p.num_rows
+    table = 0
+    if p.mode == "paged":
+        table = int(4 * np.ceil(L / p.page_size).sum())
+    meta = 4 * p.num_rows * (1 + (p.row_starts is not None) + (p.mode == "ragged"))
+    return {"score": score, "out": out, "table": table, "meta": meta,
+            "total": score + out + table + meta}
+
+
+class Runner:
+    """Device copies of one workload and a rotation of its score rows."""
+
+    def __init__(self, p, rotate: bool = True):
+        import torch
+
+        self.p = p
+        dev = torch.device("cuda")
+        self.scores0 = torch.from_numpy(p.scores).to(dev)
+        nbytes = p.scores.nbytes
+        self.copies = max(1, -(-ROTATION_BYTES // nbytes)) if rotate else 1
+        if self.copies > 1:
+            self.rot = torch.empty((self.copies,) + tuple(p.scores.shape), dtype=torch.float32,
+                                   device=dev)
+            self.rot[:] = self.scores0
+        else:
+            self.rot = self.scores0[None]
+        self.lens = torch.from_numpy(p.seq_lens).to(dev)
+        self.starts = None if p.row_starts is None else torch.from_numpy(p.row_starts).to(dev)
+        if p.mode == "ragged":
+            self.offs = torch.from_numpy(p.out_offsets).to(dev)
+        else:
+            self.pt = torch.from_numpy(p.page_table).to(dev)
+        self.out = torch.empty((p.num_rows, p.k), dtype=torch.int32, device=dev)
+        import row_top_selection_amd as dt
+
+        self.dt = dt
+        self.plan = dt.plan(self.lens, p.k)
+
+    def make_plan(self):
+        self.dt.plan(self.lens, self.p.k, out=self.plan)
+
+    def transform(self, i: int):
+        p, dt = self.p, self.dt
+        s = self.rot[i % self.copies]
+        if p.mode == "ragged":
+            dt.ragged(s, self.lens, self.offs, p.k, row_starts=self.starts, plan=self.plan,
+                      out=self.out)
+        else:
+            dt.paged(s, self.lens, self.pt, p.page_size, p.k, row_starts=self.starts,
+                     plan=self.plan, out=self.out)
+
+    def step(self, i: int):
+        self.make_plan()
+        self.transform(i)
+
+    def free(self):
+        del self.rot, self.scores0
+
+
+def time_steps(fn, steps: int, warmup: int) -> float:
+    """Seconds for `steps` calls of fn(i), bracketed by device syncs."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
+    """Mean duration of fn(i)'s launches, each bracketed by HIP events on
+    the stream the kernels are launched on (torch's current stream)."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(warmup + i)
+        b.record()
+    torch.cuda.synchronize()
+    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(p, budget_s: float = 12.0) -> dict:
+    """The oracle, as it is, on this host's cores: repeated passes over the
+    paged_decode batch until about `budget_s` of work."""
+    import oracle
+
+    orc = oracle.default()
+    threads = oracle.default_threads()
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.paged(p.scores, p.seq_lens, p.row_starts, p.page_table, p.page_size, p.k,
+                  threads=threads)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": done * p.num_rows / el,
+        "unit": "rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} passes of the oracle over the full {p.num_rows}-row paged_decode "
+                  f"batch ({el:.1f} s, {threads} threads)",
+        "score_GBps": done * algorithmic_bytes(p)["score"] / el / 1e9,
+    }
+
+
+def describe(p) -> dict:
+    L = p.window_lengths()
+    return {"rows": p.num_rows, "k": p.k, "mode": p.mode,
+            "seq_len": int(L[0]) if (L == L[0]).all() else [int(L.min()), int(L.max())]}
+
+
+def measure_workload(p, iters: int) -> dict:
+    r = Runner(p)
+    us = kernel_time_us(r.transform, iters)
+    b = algorithmic_bytes(p)
+    res = dict(describe(p), transform_us=us, rows_per_s=p.num_rows / (us * 1e-6),
+               score_GBps=b["score"] / (us * 1e3), total_GBps=b["total"] / (us * 1e3),
+               hbm_frac=b["total"] / (us * 1e3) / HBM_PEAK_GBPS, bytes=b, rotation=r.copies)
+    r.free()
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline step and roofline only")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the selection shards by rows with no exchange, "
+              "and multi-GPU runs are not part of this build (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    p = workloads.make_workload("paged_decode")
+    r = Runner(p)
+    secs = time_steps(r.step, args.steps, args.warmup)
+    ms = 1e3 * secs / args.steps
+    b = algorithmic_bytes(p)
+    k_us = kernel_time_us(r.transform, max(args.steps, 50))
+    plan_us = kernel_time_us(lambda i: r.make_plan(), 50)
+    achieved = b["total"] / (k_us * 1e3)
+    line = {
+        "metric": METRIC,
+        "value": p.num_rows * args.steps / secs,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "paged_decode: PAGED, 128 rows x 8192 fp32 N(0,1) scores, k=2048, "
+                               "page_size=64, random page tables; step = plan + paged transform",
+                   **describe(p), "page_size": p.page_size,
+                   "cold_rotation_copies": r.copies},
+        "score_GBps_step": b["score"] * args.steps / secs / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "dsatopk::rows_kernel<paged>", "kernel_us": k_us,
+                     "bytes_per_launch": b, "score_GBps": b["score"] / (k_us * 1e3),
+                     "plan_us": plan_us},
+    }
+    r.free()
+    del r
+    torch.cuda.empty_cache()
+    if not args.quick:
+        sus = {}
+        for name, mk in (("paged_decode_x32768", lambda: workloads.scaled_decode(32768)),
+                         ("paged_long_x2048", lambda: workloads.scaled_long(2048))):
+            sus[name] = measure_workload(mk(), 20)
+            torch.cuda.empty_cache()
+        line["sustained"] = sus
+        wl = {}
+        for name in workloads.WORKLOADS:
+            wl[name] = measure_workload(workloads.make_workload(name), 50)
+            torch.cuda.empty_cache()
+        line["workloads"] = wl
+    line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

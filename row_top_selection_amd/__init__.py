@@ -1,0 +1,165 @@
+"""Python binding of ``libdsatopk.so`` (the C ABI in ``include/dsatopk.h``).
+
+Argument marshalling only: every step of the selection runs in the HIP
+kernels of the library. Tensors are torch CUDA (HIP) tensors; torch is used
+for device memory and the current stream. If the library has not been
+built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libdsatopk.so"
+
+MAX_K = 2048
+MAX_SEQ_LEN = 131072
+
+STATUS = {
+    0: "DSATOPK_OK",
+    1: "DSATOPK_ERR_INVALID_ARG",
+    2: "DSATOPK_ERR_ALIGNMENT",
+    3: "DSATOPK_ERR_PLAN_TOO_SMALL",
+    4: "DSATOPK_ERR_HIP",
+}
+
+EXPORTS = ("dsatopk_status_string", "dsatopk_plan_bytes", "dsatopk_plan", "dsatopk_paged",
+           "dsatopk_ragged")
+
+
+class DsatopkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib().dsatopk_status_string(status).decode()})")
+
+
+_handle = None
+
+
+def _lib():
+    """The loaded library with argument types set (raises if not built)."""
+    global _handle
+    if _handle is None:
+        if not LIB_PATH.exists():
+            raise ImportError(f"{LIB_PATH} is not built: run row_top_selection_amd.build.build()")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.dsatopk_status_string.argtypes = [ctypes.c_int]
+        lib.dsatopk_status_string.restype = ctypes.c_char_p
+        lib.dsatopk_plan_bytes.argtypes = [i32]
+        lib.dsatopk_plan_bytes.restype = sz
+        lib.dsatopk_plan.argtypes = [P, i32, i32, P, sz, P]
+        lib.dsatopk_plan.restype = ctypes.c_int
+        lib.dsatopk_paged.argtypes = [P, i64, P, P, P, i64, i32, i32, i32, P, sz, P, P]
+        lib.dsatopk_paged.restype = ctypes.c_int
+        lib.dsatopk_ragged.argtypes = [P, i64, P, P, P, i32, i32, P, sz, P, P]
+        lib.dsatopk_ragged.restype = ctypes.c_int
+        _handle = lib
+    return _handle
+
+
+def lib():
+    """Raw ctypes handle of libdsatopk.so."""
+    return _lib()
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _vec_i32(t, n, name):
+    import torch
+
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 vector of length {n}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _scores(scores):
+    import torch
+
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a 2-D float32 tensor with contiguous columns")
+    if not scores.is_cuda:
+        raise ValueError("scores must be a device tensor")
+    return scores
+
+
+def _out(out, rows, k, like):
+    import torch
+
+    if out is None:
+        return torch.empty((rows, k), dtype=torch.int32, device=like.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape ({rows}, {k})")
+    return out
+
+
+def plan_bytes(num_rows: int) -> int:
+    return int(_lib().dsatopk_plan_bytes(int(num_rows)))
+
+
+def plan(seq_lens, k: int, out=None, stream=None):
+    """Build a plan (uint8 device tensor) from ``seq_lens`` for top-``k``."""
+    import torch
+
+    n = int(seq_lens.shape[0])
+    _vec_i32(seq_lens, n, "seq_lens")
+    nbytes = plan_bytes(n)
+    if out is None:
+        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=seq_lens.device)
+    st = _lib().dsatopk_plan(_ptr(seq_lens), n, int(k), _ptr(out), out.numel(), _stream(stream))
+    if st != 0:
+        raise DsatopkError(st, "dsatopk_plan")
+    return out
+
+
+def paged(scores, seq_lens, page_table, page_size: int, k: int, row_starts=None, plan=None,
+          out=None, stream=None):
+    """PAGED top-k: int32 ``[rows, k]`` of page-table-mapped positions."""
+    scores = _scores(scores)
+    rows = int(scores.shape[0])
+    _vec_i32(seq_lens, rows, "seq_lens")
+    _vec_i32(row_starts, rows, "row_starts")
+    if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.shape[0] != rows:
+        raise ValueError("page_table must be [rows, width] with contiguous columns")
+    out = _out(out, rows, int(k), scores)
+    st = _lib().dsatopk_paged(
+        _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
+        page_table.stride(0), int(page_size), rows, int(k), _ptr(plan),
+        0 if plan is None else plan.numel(), _ptr(out), _stream(stream))
+    if st != 0:
+        raise DsatopkError(st, "dsatopk_paged")
+    return out
+
+
+def ragged(scores, seq_lens, out_offsets, k: int, row_starts=None, plan=None, out=None,
+           stream=None):
+    """RAGGED top-k: int32 ``[rows, k]`` of position + out_offsets[row]."""
+    scores = _scores(scores)
+    rows = int(scores.shape[0])
+    _vec_i32(seq_lens, rows, "seq_lens")
+    _vec_i32(row_starts, rows, "row_starts")
+    _vec_i32(out_offsets, rows, "out_offsets")
+    out = _out(out, rows, int(k), scores)
+    st = _lib().dsatopk_ragged(
+        _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(out_offsets),
+        rows, int(k), _ptr(plan), 0 if plan is None else plan.numel(), _ptr(out),
+        _stream(stream))
+    if st != 0:
+        raise DsatopkError(st, "dsatopk_ragged")
+    return out
