@@ -76,10 +76,10 @@ class Runner:
         import row_top_selection_amd as dt
 
         self.dt = dt
-        self.plan = dt.plan(self.lens, p.k)
+        self.plan = dt.plan(self.lens, p.k, row_starts=self.starts)
 
     def make_plan(self):
-        self.dt.plan(self.lens, self.p.k, out=self.plan)
+        self.dt.plan(self.lens, self.p.k, row_starts=self.starts, out=self.plan)
 
     def transform(self, i: int):
         p, dt = self.p, self.dt

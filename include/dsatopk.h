@@ -39,8 +39,7 @@
  *     on error nothing is written and a status other than DSATOPK_OK is
  *     returned. No call aborts or throws.
  *   - The library holds no global state and is safe to call from several
- *     host threads. Two calls that share one plan buffer must not overlap
- *     in time (see dsatopk_plan).
+ *     host threads.
  */
 #ifndef DSATOPK_H_
 #define DSATOPK_H_
@@ -85,29 +84,33 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
 /*
  * dsatopk_plan - build the device-side schedule for a batch.
  *
- * Reads seq_lens[num_rows] (int32, device) and writes the plan buffer
- * (device, plan_bytes >= dsatopk_plan_bytes(num_rows), 16-byte aligned):
- * which rows are long enough to be cut into several workgroup segments and
- * how many, plus the zeroed exchange area those segments synchronise
- * through. Everything is computed on the device; nothing is read back.
+ * Reads seq_lens[num_rows] and row_starts[num_rows] (int32, device;
+ * row_starts may be NULL, meaning every window starts at column 0) and
+ * writes the plan buffer (device, plan_bytes >= dsatopk_plan_bytes(num_rows),
+ * 16-byte aligned): each row's length class (trivial or up to 8192 aligned
+ * floats, up to 16384, longer) and the list of rows of each class, so that
+ * each class's kernel runs on packed workgroups. Everything is computed on
+ * the device; nothing is read back.
  *
  * The plan only schedules: a call given a plan built from different
- * seq_lens, or no plan at all (NULL), returns the same outputs. A plan
- * must come from a dsatopk_plan call with the same num_rows and k. A plan
- * may be reused by any number of later transform calls (one per layer, say)
- * as long as those calls do not run concurrently: each call leaves the
- * exchange area zeroed again for the next one.
+ * seq_lens / row_starts / k, or no plan at all (NULL), returns the same
+ * outputs (every kernel recomputes each row's class, and a row whose class
+ * changed is served by the long-row kernel). A plan must come from a
+ * dsatopk_plan call with the same num_rows. A plan is only read by the
+ * transform calls, so it may be reused by any number of them (one per
+ * layer, say), also concurrently.
  *
  * Source: PR #26788 digest, "Key source excerpts", plan_topk_v2 (a device
  * plan built from seq_lens and reused by the transform); the layout here is
  * this library's own.
  *
  * Errors: DSATOPK_ERR_INVALID_ARG (num_rows < 0, k outside [1, 2048],
- * NULL seq_lens or plan with num_rows > 0), DSATOPK_ERR_PLAN_TOO_SMALL,
- * DSATOPK_ERR_HIP. num_rows == 0 is a no-op.
+ * NULL seq_lens or plan with num_rows > 0), DSATOPK_ERR_ALIGNMENT (plan not
+ * 16-byte aligned), DSATOPK_ERR_PLAN_TOO_SMALL, DSATOPK_ERR_HIP.
+ * num_rows == 0 is a no-op.
  */
-int dsatopk_plan(const int32_t* seq_lens, int32_t num_rows, int32_t k, void* plan,
-                 size_t plan_bytes, void* stream);
+int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num_rows, int32_t k,
+                 void* plan, size_t plan_bytes, void* stream);
 
 /*
  * dsatopk_paged - top-k with the PAGED emit.
@@ -122,7 +125,7 @@ int dsatopk_plan(const int32_t* seq_lens, int32_t num_rows, int32_t k, void* pla
  *                     position j.
  *   page_size         power of two in [1, 2^20].
  *   num_rows, k       0 <= num_rows; 1 <= k <= 2048.
- *   plan, plan_bytes  from dsatopk_plan, or NULL / 0.
+ *   plan, plan_bytes  from dsatopk_plan, or NULL / 0 (read only).
  *   out               int32 [num_rows, k], written (all of it).
  *
  * Device-side preconditions (not checkable without reading device memory,
@@ -138,7 +141,7 @@ int dsatopk_plan(const int32_t* seq_lens, int32_t num_rows, int32_t k, void* pla
 int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                   const int32_t* row_starts, const int32_t* page_table,
                   int64_t page_table_stride, int32_t page_size, int32_t num_rows, int32_t k,
-                  void* plan, size_t plan_bytes, int32_t* out, void* stream);
+                  const void* plan, size_t plan_bytes, int32_t* out, void* stream);
 
 /*
  * dsatopk_ragged - top-k with the RAGGED emit: out = j + out_offsets[b].
@@ -152,7 +155,7 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
  */
 int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                    const int32_t* row_starts, const int32_t* out_offsets, int32_t num_rows,
-                   int32_t k, void* plan, size_t plan_bytes, int32_t* out, void* stream);
+                   int32_t k, const void* plan, size_t plan_bytes, int32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

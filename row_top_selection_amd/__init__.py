@@ -48,7 +48,7 @@ def _lib():
         lib.dsatopk_status_string.restype = ctypes.c_char_p
         lib.dsatopk_plan_bytes.argtypes = [i32]
         lib.dsatopk_plan_bytes.restype = sz
-        lib.dsatopk_plan.argtypes = [P, i32, i32, P, sz, P]
+        lib.dsatopk_plan.argtypes = [P, P, i32, i32, P, sz, P]
         lib.dsatopk_plan.restype = ctypes.c_int
         lib.dsatopk_paged.argtypes = [P, i64, P, P, P, i64, i32, i32, i32, P, sz, P, P]
         lib.dsatopk_paged.restype = ctypes.c_int
@@ -113,16 +113,18 @@ def plan_bytes(num_rows: int) -> int:
     return int(_lib().dsatopk_plan_bytes(int(num_rows)))
 
 
-def plan(seq_lens, k: int, out=None, stream=None):
-    """Build a plan (uint8 device tensor) from ``seq_lens`` for top-``k``."""
+def plan(seq_lens, k: int, row_starts=None, out=None, stream=None):
+    """Build a plan (uint8 device tensor) from ``seq_lens`` / ``row_starts``."""
     import torch
 
     n = int(seq_lens.shape[0])
     _vec_i32(seq_lens, n, "seq_lens")
+    _vec_i32(row_starts, n, "row_starts")
     nbytes = plan_bytes(n)
     if out is None:
         out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=seq_lens.device)
-    st = _lib().dsatopk_plan(_ptr(seq_lens), n, int(k), _ptr(out), out.numel(), _stream(stream))
+    st = _lib().dsatopk_plan(_ptr(seq_lens), _ptr(row_starts), n, int(k), _ptr(out), out.numel(),
+                             _stream(stream))
     if st != 0:
         raise DsatopkError(st, "dsatopk_plan")
     return out

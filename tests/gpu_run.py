@@ -32,7 +32,7 @@ def run(p, d=None, use_plan=False, raw=False, canary=True):
     R, k = p.num_rows, p.k
     big = torch.full((R + 2, k), CANARY, dtype=torch.int32, device=d["scores"].device)
     out = big[1:R + 1]
-    plan = dt.plan(d["lens"], k) if use_plan else None
+    plan = dt.plan(d["lens"], k, row_starts=d["starts"]) if use_plan else None
     if raw:
         zeros = torch.zeros(R, dtype=torch.int32, device=d["scores"].device)
         dt.ragged(d["scores"], d["lens"], zeros, k, row_starts=d["starts"], plan=plan, out=out)

@@ -88,15 +88,16 @@ def test_zero_rows_is_a_noop(lib):
     # nothing is launched and no pointer is looked at
     assert paged(lib, rows=0, scores=None, lens=None, out=None, pt=None) == 0
     assert ragged(lib, rows=0, scores=None, lens=None, out=None, offs=None) == 0
-    assert lib.dsatopk_plan(None, 0, 16, None, 0, None) == 0
+    assert lib.dsatopk_plan(None, None, 0, 16, None, 0, None) == 0
 
 
 def test_plan_rejects(lib):
-    assert lib.dsatopk_plan(A16, -1, 16, A16, 1 << 20, None) == 1
-    assert lib.dsatopk_plan(A16, 4, 0, A16, 1 << 20, None) == 1
-    assert lib.dsatopk_plan(None, 4, 16, A16, 1 << 20, None) == 1
-    assert lib.dsatopk_plan(A16, 4, 16, None, 1 << 20, None) == 1
-    assert lib.dsatopk_plan(A16, 4, 16, A16, 8, None) == 3
+    assert lib.dsatopk_plan(A16, None, -1, 16, A16, 1 << 20, None) == 1
+    assert lib.dsatopk_plan(A16, None, 4, 0, A16, 1 << 20, None) == 1
+    assert lib.dsatopk_plan(None, None, 4, 16, A16, 1 << 20, None) == 1
+    assert lib.dsatopk_plan(A16, None, 4, 16, None, 1 << 20, None) == 1
+    assert lib.dsatopk_plan(A16, None, 4, 16, A16, 8, None) == 3
+    assert lib.dsatopk_plan(A16, None, 4, 16, A4, 1 << 20, None) == 2
 
 
 def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
