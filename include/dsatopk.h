@@ -58,7 +58,7 @@ enum {
        score_stride < 1; page_size not a power of two in [1, 2^20];
        page_table_stride < 1. */
     DSATOPK_ERR_INVALID_ARG = 1,
-    /* scores not 16-byte aligned, or score_stride not a multiple of 4. */
+    /* scores or plan not 16-byte aligned, or score_stride not a multiple of 4. */
     DSATOPK_ERR_ALIGNMENT = 2,
     /* plan_bytes smaller than dsatopk_plan_bytes(num_rows). */
     DSATOPK_ERR_PLAN_TOO_SMALL = 3,
@@ -89,16 +89,20 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  * writes the plan buffer (device, plan_bytes >= dsatopk_plan_bytes(num_rows),
  * 16-byte aligned): each row's length class (trivial or up to 8192 aligned
  * floats, up to 16384, longer) and the list of rows of each class, so that
- * each class's kernel runs on packed workgroups. Everything is computed on
- * the device; nothing is read back.
+ * each class's kernel runs on packed workgroups; and, for up to 512 rows
+ * longer than 16384, a cut into segments of 8192 floats served by one
+ * workgroup each, with a zeroed exchange area per row through which the
+ * segments merge their histograms. Everything is computed on the device;
+ * nothing is read back.
  *
  * The plan only schedules: a call given a plan built from different
  * seq_lens / row_starts / k, or no plan at all (NULL), returns the same
- * outputs (every kernel recomputes each row's class, and a row whose class
- * changed is served by the long-row kernel). A plan must come from a
- * dsatopk_plan call with the same num_rows. A plan is only read by the
- * transform calls, so it may be reused by any number of them (one per
- * layer, say), also concurrently.
+ * outputs (every kernel recomputes each row's class and segment count, and
+ * a row that no longer matches its plan is served by the streaming
+ * long-row kernel). A plan must come from a dsatopk_plan call with the same
+ * num_rows. A plan may be reused by any number of later transform calls
+ * (one per layer, say): each call leaves the exchange areas zeroed again.
+ * Calls that share one plan must not run concurrently.
  *
  * Source: PR #26788 digest, "Key source excerpts", plan_topk_v2 (a device
  * plan built from seq_lens and reused by the transform); the layout here is
@@ -125,7 +129,8 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
  *                     position j.
  *   page_size         power of two in [1, 2^20].
  *   num_rows, k       0 <= num_rows; 1 <= k <= 2048.
- *   plan, plan_bytes  from dsatopk_plan, or NULL / 0 (read only).
+ *   plan, plan_bytes  from dsatopk_plan, or NULL / 0. Its exchange areas are
+ *                     written during the call and left zeroed.
  *   out               int32 [num_rows, k], written (all of it).
  *
  * Device-side preconditions (not checkable without reading device memory,
@@ -141,7 +146,7 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
 int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                   const int32_t* row_starts, const int32_t* page_table,
                   int64_t page_table_stride, int32_t page_size, int32_t num_rows, int32_t k,
-                  const void* plan, size_t plan_bytes, int32_t* out, void* stream);
+                  void* plan, size_t plan_bytes, int32_t* out, void* stream);
 
 /*
  * dsatopk_ragged - top-k with the RAGGED emit: out = j + out_offsets[b].
@@ -155,7 +160,7 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
  */
 int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                    const int32_t* row_starts, const int32_t* out_offsets, int32_t num_rows,
-                   int32_t k, const void* plan, size_t plan_bytes, int32_t* out, void* stream);
+                   int32_t k, void* plan, size_t plan_bytes, int32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,7 +58,7 @@ struct Params {
   int32_t num_rows;
   int32_t k;
   int32_t* out;
-  const int32_t* plan;  // plan words (header, class lists, classes) or null
+  int32_t* plan;  // plan words (header, class lists, classes, exchange areas) or null
 };
 
 // Row classes by aligned span. A row's class is recomputed by every kernel
@@ -76,7 +76,56 @@ enum PlanWord : int32_t {
   kPlanWordK = 2,
   kPlanWordCount = 4,   // [3] rows per class
   kPlanWordOffset = 8,  // [3] first list index per class
+  kPlanWordSplit = 12,  // long rows cut into segments (each owns an exchange area)
+  kPlanWordItems = 13,  // (row, segment) work items of those rows
+  kPlanWordError = 14,  // set if a segment ever gave up waiting (never, if correct)
 };
+
+// Long rows are cut into segments of kSegLen aligned floats, one workgroup
+// each, holding its segment in registers like a short row. The segments of
+// a row merge their digit histograms through the row's exchange area in
+// the plan buffer (this replaces the pages' thread-block cluster path:
+// CDNA has no clusters or distributed shared memory).
+constexpr int kSegLen = kSmallVec * 4 * kBlock;                                  // 8192
+constexpr int kMaxSeg = (DSATOPK_MAX_SEQ_LEN + 3 + kSegLen - 1) / kSegLen;         // 17
+constexpr int kMaxSplitRows = 512;
+constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
+
+// Exchange area of one split row (int32 words). Every region is zero at
+// the start of a call; the last segment to finish re-zeroes what the call
+// used.
+constexpr int kCandCapG = 2048;  // threshold-bin elements resolved by one wave
+enum XWord : int32_t {
+  kXA = 0,              // 4096 bins: key bits 31..20
+  kXCand = 4096,        // kCandCapG (key, position) pairs of the level-1 bin
+  kXB = 8192,           // fallback digits: 4096 bins, key bits 19..8
+  kXC = 12288,          // 256 bins: key bits 7..0
+  kXD = 12544,          // 4096 bins: position bits 16..5
+  kXE = 16640,          // 32 bins: position bits 4..0
+  kXFlag = 16672,       // 64-bit: last published round and its result
+  kXArrive = 16674,     // segments arrived (all rounds)
+  kXNCand = 16675,      // candidate pairs written
+  kXOut = 16676,        // output slots taken
+  kXDone = 16677,       // segments finished
+  kXFallback = 16678,   // the fallback digits were used
+  kXWords = 16704,      // multiple of 64 words (256 bytes)
+};
+
+__host__ __device__ constexpr int64_t plan_split_cap(int64_t rows) {
+  return rows < kMaxSplitRows ? rows : kMaxSplitRows;
+}
+__host__ __device__ constexpr int64_t plan_nseg_word(int64_t rows) { return kPlanHeaderWords + 2 * rows; }
+__host__ __device__ constexpr int64_t plan_slot_word(int64_t rows) { return kPlanHeaderWords + 3 * rows; }
+__host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
+__host__ __device__ constexpr int64_t plan_xarea_word(int64_t rows) {
+  return (plan_items_word(rows) + 2 * plan_split_cap(rows) * kMaxSeg + 63) / 64 * 64;
+}
+__host__ __device__ constexpr int64_t plan_words(int64_t rows) {
+  return plan_xarea_word(rows) + plan_split_cap(rows) * kXWords;
+}
+__host__ __device__ constexpr int32_t segments_for(int32_t span) {
+  return (span + kSegLen - 1) / kSegLen;
+}
 
 // Output of one row: window position j -> emitted value. In PAGED mode the
 // row's page-table entries may be staged in LDS first (short windows).
@@ -84,14 +133,15 @@ template <bool kPaged>
 struct Emit {
   int32_t* out;
   const int32_t* pt;      // the row's page-table entries (global)
-  const int32_t* pt_lds;  // staged copy, or null
+  const int32_t* pt_lds;  // staged copy of entries pt_first.., or null
+  int32_t pt_first;
   int32_t page_bits;
   int32_t offset;
 
   __device__ __forceinline__ int32_t value(int32_t j) const {
     if constexpr (kPaged) {
       const int32_t e = j >> page_bits;
-      const int32_t page = pt_lds ? pt_lds[e] : pt[e];
+      const int32_t page = pt_lds ? pt_lds[e - pt_first] : pt[e];
       return (int32_t)(((uint32_t)page << page_bits) | ((uint32_t)j & ((1u << page_bits) - 1u)));
     } else {
       return j + offset;
@@ -101,11 +151,21 @@ struct Emit {
   // Stage the first ceil(L / page_size) table entries into `lds` when they
   // fit; issued early so the loads overlap the score loads.
   __device__ __forceinline__ void stage_table(int32_t* lds, int32_t L) {
+    stage_table_range(lds, 0, L);
+  }
+
+  // Same for the entries of window positions [j0, j1) only (clamped to the
+  // window [0, L)).
+  __device__ __forceinline__ void stage_table_range(int32_t* lds, int32_t j0, int32_t j1) {
     if constexpr (kPaged) {
-      const int32_t n = (int32_t)(((uint32_t)L + (1u << page_bits) - 1u) >> page_bits);
+      j0 = j0 < 0 ? 0 : j0;
+      if (j1 <= j0) return;
+      const int32_t e0 = j0 >> page_bits;
+      const int32_t n = ((j1 - 1) >> page_bits) - e0 + 1;
       if (n <= kPtCap) {
-        for (int32_t e = threadIdx.x; e < n; e += kBlock) lds[e] = pt[e];
+        for (int32_t e = threadIdx.x; e < n; e += kBlock) lds[e] = pt[e0 + e];
         pt_lds = lds;
+        pt_first = e0;
       }
     }
   }
@@ -154,13 +214,13 @@ __device__ __forceinline__ float lane_of(const float4& v, int c) {
 template <int NV>
 struct RegSrc {
   const uint32_t (&key)[NV][4];
-  int32_t rem;
+  int32_t origin;  // window position of register element (0, 0) of thread 0
 
   // Positions are rebuilt from one opaque base in every pass: the compiler
   // cannot keep NV * 4 position registers alive across passes.
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
-    int32_t base = (int32_t)threadIdx.x * 4 - rem;
+    int32_t base = (int32_t)threadIdx.x * 4 + origin;
     asm volatile("" : "+v"(base));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -369,7 +429,7 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
     }
   }
   __syncthreads();
-  const RegSrc<NV> src{key, rv.rem};
+  const RegSrc<NV> src{key, -rv.rem};
   const Cut cut = refine_in_registers(src, sm, (uint32_t)k);
 
   // Selection becomes one compare, key >= thr. Without a partial tie class
@@ -480,6 +540,7 @@ __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b) {
   em.out = p.out + b * p.k;
   em.page_bits = p.page_bits;
   em.pt_lds = nullptr;
+  em.pt_first = 0;
   if constexpr (kPaged) {
     em.pt = p.page_table + b * p.pt_stride;
     em.offset = 0;
@@ -570,15 +631,25 @@ __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
   row_in_registers<kLargeVec>(row_view(p, b, r), p.k, row_emit<kPaged>(p, b), sm);
 }
 
-// Longer spans, streamed; also any row whose class differs from the plan's
-// (such a row is skipped by the other launches). One workgroup per row.
+// Whether row b is served by the split kernel: it was planned as a split
+// row and still has the planned number of segments.
+__device__ __forceinline__ bool split_served(const Params& p, int64_t b, const RowInfo& r) {
+  if (!plan_ok(p) || r.cls != kClassLong) return false;
+  const int32_t S = p.plan[plan_nseg_word(p.num_rows) + b];
+  const int32_t slot = p.plan[plan_slot_word(p.num_rows) + b];
+  return S >= 2 && S == segments_for(r.span) && slot >= 0 && slot < plan_split_cap(p.num_rows);
+}
+
+// Longer spans, streamed, one workgroup per row: long rows the split kernel
+// does not serve, and any row whose class differs from the plan's (such a
+// row is skipped by the other launches).
 template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
   const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
   const int32_t* planned = plan_ok(p) ? p.plan + kPlanHeaderWords + p.num_rows : nullptr;
   const bool stale = planned && planned[b] != r.cls;
-  if (r.cls != kClassLong && !stale) return;
+  if (!((r.cls == kClassLong && !split_served(p, b, r)) || stale)) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
     write_trivial(em, r.L, p.k);
@@ -586,6 +657,445 @@ __global__ __launch_bounds__(kBlock) void rows_long_kernel(const Params p) {
   }
   __shared__ SmemStream sm;
   row_streaming(row_view(p, b, r), p.k, em, sm);
+}
+
+// A published round result: round number in bits 63..56, the payload in
+// the low 56 bits (a bin search: bin << 36 | before << 18 | count, each
+// count < 2^18; a resolved cut: pos << 32 | tau, pos = 0x3ffff for "all").
+__device__ __forceinline__ uint64_t pack_round(uint32_t round, uint64_t payload) {
+  return ((uint64_t)round << 56) | payload;
+}
+__device__ __forceinline__ uint64_t pack_hit(const BinHit& h) {
+  return ((uint64_t)h.bin << 36) | ((uint64_t)h.before << 18) | (uint64_t)h.cnt;
+}
+__device__ __forceinline__ BinHit unpack_hit(uint64_t w) {
+  BinHit h;
+  h.bin = (uint32_t)(w >> 36) & 0xfffffu;
+  h.before = (uint32_t)(w >> 18) & 0x3ffffu;
+  h.cnt = (uint32_t)w & 0x3ffffu;
+  return h;
+}
+constexpr uint32_t kPackAllPos = 0x3ffffu;
+
+// Split-row synchronisation. Every access to a row's exchange area is a
+// device-scope atomic (read-modify-write, load or store), and device-scope
+// atomics are coherent across the chip's XCDs; none of them needs the L2
+// write-back or invalidation that release / acquire fences would add at
+// every round. Ordering comes from waiting: before a segment arrives, each
+// of its waves waits until its own atomics have completed, so whoever sees
+// the arrival count complete also sees every contribution. Every segment
+// arrives once per round; the last to arrive computes the round's result
+// and publishes it in one 64-bit word, which the others poll. Polls are
+// bounded: a segment that gives up sets the plan's error word and goes on
+// with whatever it read, so no wave can hang.
+//
+// Forward progress: the segments of a row are consecutive work items, i.e.
+// consecutive workgroups; workgroups are dispatched in order, and a row
+// has at most kMaxSeg of them, far fewer than the workgroups that fit on
+// the chip, so the missing segments of a waiting row are always
+// dispatchable.
+struct SplitSync {
+  uint32_t* x;
+  int32_t S;
+  int32_t* err;
+  uint32_t* s_word;  // LDS: 2 words
+
+  // Returns true in the last segment to arrive at `round` (whole workgroup).
+  __device__ __forceinline__ bool arrive(uint32_t round) const {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's atomics completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&x[kXArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_word[0] = prev == (uint32_t)S * round - 1u;
+    }
+    __syncthreads();
+    return s_word[0] != 0u;
+  }
+
+  // Last arriver: make `payload` the result of `round`.
+  __device__ __forceinline__ void publish(uint32_t round, uint64_t payload) const {
+    if (threadIdx.x == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(x + kXFlag), pack_round(round, payload),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // Everyone: the published result of `round` (the last arriver passes
+  // `mine`, which it just published).
+  __device__ __forceinline__ uint64_t result(uint32_t round, bool last, uint64_t mine) const {
+    if (threadIdx.x == 0) {
+      uint64_t w = mine;
+      if (!last) {
+        const uint64_t* f = reinterpret_cast<const uint64_t*>(x + kXFlag);
+        uint32_t n = 0;
+        while (((w = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 56) <
+               round) {
+          if (++n > kSpinLimit) {
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      s_word[0] = (uint32_t)w;
+      s_word[1] = (uint32_t)(w >> 32);
+    }
+    __syncthreads();
+    const uint64_t w = ((uint64_t)s_word[1] << 32) | s_word[0];
+    __syncthreads();  // s_word may be reused right away
+    return w & ((1ull << 56) - 1ull);
+  }
+};
+
+// One histogram round: every segment adds its local LDS histogram (NB
+// bins) into the row's global one; the last to arrive gathers the totals
+// into its LDS (one coalesced read) and finds the bin where the running
+// count reaches `need`.
+template <int NB, bool kDesc>
+__device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
+                                                  uint32_t round, uint32_t need,
+                                                  const SplitSync& sy) {
+  const int32_t t = threadIdx.x;
+  __syncthreads();  // local histogram complete
+  for (int32_t i = t; i < NB; i += kBlock) {
+    const uint32_t v = lds_hist[i];
+    if (v) __hip_atomic_fetch_add(&g_hist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const bool last = sy.arrive(round);
+  uint64_t mine = 0;
+  if (last) {
+    for (int32_t i = t; i < NB; i += kBlock)
+      lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    mine = pack_hit(wave_find<NB, kDesc>(lds_hist, need));
+    sy.publish(round, mine);
+  }
+  return unpack_hit(sy.result(round, last, mine));
+}
+
+// The exact cut among n (key, position) pairs in LDS, all inside one
+// level-1 bin, taking `need` of them: key digits 19..12, 11..4, 3..0 and,
+// for ties at the k-th key, position digits 16..9, 8..1, 0. One wave, no
+// workgroup barriers; h2 / h3 / h4 are scratch histograms. Returns
+// (tau, pos): select key > tau, or key == tau and position <= pos.
+__device__ __forceinline__ uint64_t resolve_pairs_wave(const uint2* cand, uint32_t n,
+                                                       uint32_t prefix, uint32_t need,
+                                                       SmemReg& sm) {
+  const int lane = lane_id();
+  uint32_t pbits = 12;  // key bits fixed so far (from the top)
+  const uint32_t key_shift[3] = {12, 4, 0};
+  const uint32_t key_width[3] = {8, 8, 4};
+  uint32_t* hs[3] = {sm.h2, sm.h3, sm.h4};
+  uint32_t tau = 0;
+  bool resolved = false;
+  uint32_t shift_done = 20;
+  for (int d = 0; d < 3; ++d) {
+    const uint32_t sh = key_shift[d];
+    const uint32_t wd = key_width[d];
+    uint32_t* h = hs[d];
+    for (uint32_t i = lane; i < (1u << wd); i += 64) h[i] = 0;
+    wave_lds_sync();
+    const uint32_t hi_shift = sh + wd;
+    for (uint32_t i = lane; i < n; i += 64) {
+      const uint32_t kk = cand[i].x;
+      if ((kk >> hi_shift) == prefix) lds_inc(&h[(kk >> sh) & ((1u << wd) - 1u)]);
+    }
+    wave_lds_sync();
+    const BinHit b = wd == 8 ? wave_find<256, true>(h, need) : wave_find<16, true>(h, need);
+    need -= b.before;
+    prefix = (prefix << wd) | b.bin;
+    pbits += wd;
+    shift_done = sh;
+    if (b.cnt == need) {
+      resolved = true;
+      break;
+    }
+  }
+  if (resolved) {
+    // every element of the final bin is taken: its lowest key is the cut,
+    // with all ties at it taken
+    const uint32_t lo = prefix << shift_done;
+    tau = lo ? lo - 1u : 0u;  // select key > lo - 1, i.e. key >= lo
+    return ((uint64_t)kPackAllPos << 32) | tau;
+  }
+  tau = prefix;  // all 32 key bits
+  // ties: the need lowest positions among key == tau
+  uint32_t pprefix = 0;
+  const uint32_t pos_shift[3] = {9, 1, 0};
+  const uint32_t pos_width[3] = {8, 8, 1};
+  for (int d = 0; d < 3; ++d) {
+    const uint32_t sh = pos_shift[d];
+    const uint32_t wd = pos_width[d];
+    uint32_t* h = hs[d];
+    wave_lds_sync();
+    for (uint32_t i = lane; i < (1u << wd); i += 64) h[i] = 0;
+    wave_lds_sync();
+    const uint32_t hi_shift = sh + wd;
+    for (uint32_t i = lane; i < n; i += 64) {
+      const uint2 e = cand[i];
+      if ((e.x == tau) & ((e.y >> hi_shift) == pprefix))
+        lds_inc(&h[(e.y >> sh) & ((1u << wd) - 1u)]);
+    }
+    wave_lds_sync();
+    const BinHit b = wd == 8 ? wave_find<256, false>(h, need) : wave_find<2, false>(h, need);
+    need -= b.before;
+    pprefix = (pprefix << wd) | b.bin;
+  }
+  return ((uint64_t)pprefix << 32) | (tau - 1u);  // key > tau - 1 and pos cut
+}
+
+// One segment of a split row: the segment sits in registers like a short
+// row; the level-1 histogram is merged over the row in one round; the
+// level-1 bin's elements of the whole row (at most kCandCapG) then go to
+// the row's candidate buffer, and the last segment to arrive resolves the
+// exact cut from them (second round). A level-1 bin too large for the
+// buffer falls back to one round per further digit (12 and 8 key bits, 12
+// and 5 position bits). Output slots come from the row's shared counter.
+template <bool kPaged>
+__device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b, const RowInfo& r,
+                                                     int32_t seg, int32_t S, uint32_t* x,
+                                                     SmemReg& sm, uint32_t* s_word) {
+  constexpr int NV = kSmallVec;
+  const int32_t t = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const uint32_t k = (uint32_t)p.k;
+  const SplitSync sy{x, S, p.plan + kPlanWordError, s_word};
+  const int32_t rem = r.s & 3;
+  const float4* base4 = reinterpret_cast<const float4*>(p.scores + b * p.stride + (r.s - rem));
+  const int32_t nvec = (r.span + 3) >> 2;
+  const int32_t v0 = seg * (kSegLen / 4);  // first aligned vector of the segment
+  Emit<kPaged> em = row_emit<kPaged>(p, b);
+  uint32_t key[NV][4];
+  {
+    float4 xv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int32_t v = v0 + i * kBlock + t;
+      xv[i] = v < nvec ? base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int32_t j0 = v0 * 4 - rem;
+    const int32_t j1 = j0 + kSegLen < r.L ? j0 + kSegLen : r.L;
+    em.stage_table_range(sm.pt, j0, j1);
+    clear_bins<kBins>(sm.hist);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int32_t v = v0 + i * kBlock + t;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(xv[i], c));
+      if ((v == 0) | (v * 4 + 4 > r.span)) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int32_t a = v * 4 + c;
+          if ((a < rem) | (a >= r.span)) key[i][c] = 0;
+        }
+      }
+    }
+  }
+  const RegSrc<NV> src{key, v0 * 4 - rem};
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (v0 + i * kBlock + t < nvec) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lds_inc(&sm.hist[key[i][c] >> 20]);
+    }
+  }
+  uint32_t round = 1;
+  BinHit h = histogram_round<kBins, true>(sm.hist, x + kXA, round++, k, sy);
+  uint32_t need = k - h.before;
+  Cut cut{20, h.bin, kAllPos};
+  if (h.cnt != need && h.cnt <= (uint32_t)kCandCapG) {
+    // Round 2: the level-1 bin's elements of the whole row.
+    const uint32_t lo = h.bin << 20;
+    uint32_t mine = 0;
+    src.for_each([&](uint32_t kk, int32_t) { mine += ((kk - lo) < (1u << 20)) ? 1u : 0u; });
+    const uint32_t incl = wave_inclusive_sum(mine);
+    if (lane == 63) sm.wave_cnt[w] = incl;
+    __syncthreads();
+    uint32_t pre = incl - mine;
+    uint32_t tot = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      pre += v < w ? sm.wave_cnt[v] : 0u;
+      tot += sm.wave_cnt[v];
+    }
+    if (t == 0)
+      s_word[0] = __hip_atomic_fetch_add(&x[kXNCand], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    uint32_t at = s_word[0] + pre;
+    __syncthreads();
+    uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
+    src.for_each([&](uint32_t kk, int32_t j) {
+      if ((kk - lo) < (1u << 20)) {
+        if (at < (uint32_t)kCandCapG)
+          __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        ++at;
+      }
+    });
+    const bool last = sy.arrive(round);
+    uint64_t res = 0;
+    if (last) {
+      uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // 2048 pairs fit 4096 words
+      for (uint32_t i = t; i < h.cnt; i += kBlock) {
+        const uint64_t e = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+      }
+      __syncthreads();
+      if (w == 0) res = resolve_pairs_wave(lcand, h.cnt, h.bin, need, sm);
+      if (t == 0) s_word[0] = (uint32_t)res, s_word[1] = (uint32_t)(res >> 32);
+      __syncthreads();
+      res = ((uint64_t)s_word[1] << 32) | s_word[0];
+      __syncthreads();
+      sy.publish(round, res);
+    }
+    res = sy.result(round, last, res);
+    ++round;
+    const uint32_t tau1 = (uint32_t)res;  // select key > tau1 (or == tau1 + 1 up to pos)
+    const uint32_t pos = (uint32_t)(res >> 32) & kPackAllPos;
+    if (pos == kPackAllPos) {
+      cut = Cut{0, tau1 + 1u, kAllPos};  // key >= tau1 + 1
+    } else {
+      cut = Cut{0, tau1 + 1u, (int32_t)pos};
+    }
+  } else if (h.cnt != need) {
+    // Fallback: one round per further digit.
+    if (t == 0)
+      __hip_atomic_store(&x[kXFallback], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    clear_bins<kBins>(sm.hist);
+    __syncthreads();
+    {
+      const uint32_t pre = cut.prefix;
+      src.for_each([&](uint32_t kk, int32_t) {
+        if ((kk >> 20) == pre) lds_inc(&sm.hist[(kk >> 8) & 0xfffu]);
+      });
+    }
+    h = histogram_round<kBins, true>(sm.hist, x + kXB, round++, need, sy);
+    need -= h.before;
+    cut = Cut{8, (cut.prefix << 12) | h.bin, kAllPos};
+    if (h.cnt != need) {
+      sm.h2[t] = 0;
+      __syncthreads();
+      {
+        const uint32_t pre = cut.prefix;
+        src.for_each([&](uint32_t kk, int32_t) {
+          if ((kk >> 8) == pre) lds_inc(&sm.h2[kk & 0xffu]);
+        });
+      }
+      h = histogram_round<256, true>(sm.h2, x + kXC, round++, need, sy);
+      need -= h.before;
+      cut = Cut{0, (cut.prefix << 8) | h.bin, kAllPos};
+      if (h.cnt != need) {
+        const uint32_t tau = cut.prefix;
+        clear_bins<kBins>(sm.hist);
+        __syncthreads();
+        src.for_each([&](uint32_t kk, int32_t j) {
+          if (kk == tau) lds_inc(&sm.hist[(uint32_t)j >> 5]);
+        });
+        h = histogram_round<kBins, false>(sm.hist, x + kXD, round++, need, sy);
+        need -= h.before;
+        const uint32_t hi = h.bin;
+        sm.h2[t] = 0;
+        __syncthreads();
+        src.for_each([&](uint32_t kk, int32_t j) {
+          if ((kk == tau) & (((uint32_t)j >> 5) == hi)) lds_inc(&sm.h2[(uint32_t)j & 31u]);
+        });
+        h = histogram_round<32, false>(sm.h2, x + kXE, round++, need, sy);
+        cut.pos = (int32_t)((hi << 5) | h.bin);
+      }
+    }
+  }
+
+  // One compare per element (ties folded in as in the register path).
+  uint32_t thr;
+  if (cut.pos == kAllPos) {
+    const uint32_t lo = cut.prefix << cut.shift;
+    thr = lo ? lo : 1u;
+  } else {
+    const uint32_t tau = cut.prefix;
+    const int32_t pos = cut.pos;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int32_t j = (v0 + i * kBlock + t) * 4 + c - rem;
+        if ((key[i][c] == tau) & (j <= pos)) key[i][c] = tau + 1u;
+      }
+    }
+    thr = tau + 1u;
+  }
+  uint32_t mine = 0;
+  src.for_each([&](uint32_t kk, int32_t) { mine += (kk >= thr) ? 1u : 0u; });
+  const uint32_t mine_incl = wave_inclusive_sum(mine);
+  if (lane == 63) sm.wave_cnt[w] = mine_incl;
+  __syncthreads();
+  uint32_t slot = mine_incl - mine;
+  uint32_t total = 0;
+  for (int v = 0; v < kWaves; ++v) {
+    const uint32_t c = sm.wave_cnt[v];
+    slot += v < w ? c : 0u;
+    total += c;
+  }
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  const uint32_t dummy = (uint32_t)kMaxK + (uint32_t)t;
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool sel = kk >= thr;
+    stage[(sel & (slot < (uint32_t)kMaxK)) ? slot : dummy] = j;
+    slot += sel ? 1u : 0u;
+  });
+  if (t == 0)
+    s_word[0] = __hip_atomic_fetch_add(&x[kXOut], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t base = s_word[0];
+  for (uint32_t i = t; i < total; i += kBlock) {
+    const int32_t j = stage[i];
+    const bool ok = (j >= 0) & (j < r.L) & (base + i < k);
+    if (ok) em.out[base + i] = em.value(j);
+  }
+  __syncthreads();  // s_word is reused below
+  if (t == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t d =
+        __hip_atomic_fetch_add(&x[kXDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_word[0] = d == (uint32_t)S - 1u;
+  }
+  __syncthreads();
+  if (s_word[0]) {
+    // every segment is past its last access: zero what this call used
+    const bool fb =
+        __hip_atomic_load(&x[kXFallback], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    const int32_t end = fb ? kXWords : kXCand;  // the level-1 histogram, or everything
+    for (int32_t i = t; i < end; i += kBlock)
+      if (i < kXCand || i >= kXB)
+        __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int32_t i = kXFlag + t; i < kXWords; i += kBlock)
+      __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Long rows planned as split rows: one workgroup per (row, segment) item.
+template <bool kPaged>
+__global__ __launch_bounds__(kBlock) void rows_split_kernel(const Params p) {
+  if (!plan_ok(p)) return;
+  const int64_t R = p.num_rows;
+  const uint32_t it = blockIdx.x;
+  const int32_t n_items = p.plan[kPlanWordItems];
+  if ((int32_t)it >= n_items || it >= (uint32_t)(plan_split_cap(R) * kMaxSeg)) return;
+  const int32_t* items = p.plan + plan_items_word(R);
+  const int64_t b = items[2 * it];
+  const int32_t seg = items[2 * it + 1];
+  if ((uint64_t)b >= (uint64_t)R) return;
+  const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
+  if (!split_served(p, b, r)) return;
+  const int32_t S = p.plan[plan_nseg_word(R) + b];
+  if (seg < 0 || seg >= S) return;
+  const int32_t slot = p.plan[plan_slot_word(R) + b];
+  uint32_t* x = reinterpret_cast<uint32_t*>(p.plan + plan_xarea_word(R) + (int64_t)slot * kXWords);
+  __shared__ SmemReg sm;
+  __shared__ uint32_t s_word[2];
+  segment_in_registers<kPaged>(p, b, r, seg, S, x, sm, s_word);
 }
 
 // Plan: classify every row and list the rows of each class. One workgroup.
@@ -597,16 +1107,42 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
                                                          int32_t* plan) {
   __shared__ uint32_t count[3];
   __shared__ uint32_t fill[3];
+  __shared__ uint32_t n_split;
+  __shared__ uint32_t n_items;
   if (threadIdx.x < 3) {
     count[threadIdx.x] = 0;
     fill[threadIdx.x] = 0;
   }
+  if (threadIdx.x == 0) {
+    n_split = 0;
+    n_items = 0;
+  }
   __syncthreads();
   int32_t* cls = plan + kPlanHeaderWords + num_rows;
+  int32_t* nseg = plan + plan_nseg_word(num_rows);
+  int32_t* slot = plan + plan_slot_word(num_rows);
+  int32_t* items = plan + plan_items_word(num_rows);
+  const uint32_t cap = (uint32_t)plan_split_cap(num_rows);
   for (int32_t b = threadIdx.x; b < num_rows; b += kPlanBlock) {
-    const int32_t c = row_info(seq_lens, row_starts, k, b).cls;
-    cls[b] = c;
-    atomicAdd(&count[c], 1u);
+    const RowInfo r = row_info(seq_lens, row_starts, k, b);
+    cls[b] = r.cls;
+    atomicAdd(&count[r.cls], 1u);
+    int32_t S = 0;
+    int32_t q = -1;
+    if (r.cls == kClassLong) {
+      const uint32_t i = atomicAdd(&n_split, 1u);
+      if (i < cap) {
+        S = segments_for(r.span);
+        q = (int32_t)i;
+        const uint32_t at = atomicAdd(&n_items, (uint32_t)S);
+        for (int32_t sg = 0; sg < S; ++sg) {
+          items[2 * (at + sg)] = b;
+          items[2 * (at + sg) + 1] = sg;
+        }
+      }
+    }
+    nseg[b] = S;
+    slot[b] = q;
   }
   __syncthreads();
   const uint32_t off[3] = {0u, count[0], count[0] + count[1]};
@@ -623,7 +1159,18 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
       plan[kPlanWordCount + c] = (int32_t)count[c];
       plan[kPlanWordOffset + c] = (int32_t)off[c];
     }
+    plan[kPlanWordSplit] = (int32_t)(n_split < cap ? n_split : cap);
+    plan[kPlanWordItems] = (int32_t)n_items;
+    plan[kPlanWordError] = 0;
   }
+}
+
+// Zero the exchange areas of the planned split rows (one workgroup each).
+__global__ __launch_bounds__(kBlock) void plan_clear_kernel(int32_t num_rows, int32_t* plan) {
+  const int32_t q = blockIdx.x;
+  if (q >= plan[kPlanWordSplit]) return;
+  int32_t* x = plan + plan_xarea_word(num_rows) + (int64_t)q * kXWords;
+  for (int32_t i = threadIdx.x; i < kXWords; i += kBlock) x[i] = 0;
 }
 
 }  // namespace dsatopk
@@ -648,6 +1195,7 @@ int check_common(const float* scores, int64_t score_stride, const int32_t* seq_l
   if (!scores || !seq_lens || !out || score_stride < 1) return DSATOPK_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0 || (score_stride & 3) != 0)
     return DSATOPK_ERR_ALIGNMENT;
+  if (plan && (reinterpret_cast<uintptr_t>(plan) & 15u) != 0) return DSATOPK_ERR_ALIGNMENT;
   if (plan && plan_bytes < dsatopk_plan_bytes(num_rows)) return DSATOPK_ERR_PLAN_TOO_SMALL;
   return DSATOPK_OK;
 }
@@ -663,6 +1211,10 @@ int launch_rows(Params p, hipStream_t stream) {
   const bool mid = p.stride > (int64_t)kSmallVec * 4 * kBlock;
   const bool lng = p.stride > (int64_t)kLargeVec * 4 * kBlock;
   if (!lng) p.plan = nullptr;
+  if (lng && p.plan) {
+    const dim3 items((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg));
+    hipLaunchKernelGGL((rows_split_kernel<kPaged>), items, block, 0, stream, p);
+  }
   if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, block, 0, stream, p);
   hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
   if (mid) hipLaunchKernelGGL((rows_mid_kernel<kPaged>), grid, block, 0, stream, p);
@@ -686,7 +1238,7 @@ const char* dsatopk_status_string(int status) {
 
 size_t dsatopk_plan_bytes(int32_t num_rows) {
   if (num_rows < 0) return 0;
-  return sizeof(int32_t) * ((size_t)kPlanHeaderWords + 2u * (size_t)num_rows);
+  return sizeof(int32_t) * (size_t)plan_words(num_rows);
 }
 
 int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num_rows, int32_t k,
@@ -698,13 +1250,15 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
   if ((reinterpret_cast<uintptr_t>(plan) & 15u) != 0) return DSATOPK_ERR_ALIGNMENT;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanBlock), 0, (hipStream_t)stream, seq_lens,
                      row_starts, num_rows, k, (int32_t*)plan);
+  hipLaunchKernelGGL(plan_clear_kernel, dim3((unsigned)plan_split_cap(num_rows)), dim3(kBlock), 0,
+                     (hipStream_t)stream, num_rows, (int32_t*)plan);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }
 
 int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                   const int32_t* row_starts, const int32_t* page_table,
                   int64_t page_table_stride, int32_t page_size, int32_t num_rows, int32_t k,
-                  const void* plan, size_t plan_bytes, int32_t* out, void* stream) {
+                  void* plan, size_t plan_bytes, int32_t* out, void* stream) {
   int st = check_common(scores, score_stride, seq_lens, num_rows, k, out, plan, plan_bytes);
   if (st != DSATOPK_OK || num_rows == 0) return st;
   if (!page_table || page_table_stride < 1 || !is_pow2(page_size) || page_size > (1 << 20))
@@ -721,13 +1275,13 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
   p.num_rows = num_rows;
   p.k = k;
   p.out = out;
-  p.plan = (const int32_t*)plan;
+  p.plan = (int32_t*)plan;
   return launch_rows<true>(p, (hipStream_t)stream);
 }
 
 int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                    const int32_t* row_starts, const int32_t* out_offsets, int32_t num_rows,
-                   int32_t k, const void* plan, size_t plan_bytes, int32_t* out, void* stream) {
+                   int32_t k, void* plan, size_t plan_bytes, int32_t* out, void* stream) {
   int st = check_common(scores, score_stride, seq_lens, num_rows, k, out, plan, plan_bytes);
   if (st != DSATOPK_OK || num_rows == 0) return st;
   if (!out_offsets) return DSATOPK_ERR_INVALID_ARG;
@@ -743,7 +1297,7 @@ int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq
   p.num_rows = num_rows;
   p.k = k;
   p.out = out;
-  p.plan = (const int32_t*)plan;
+  p.plan = (int32_t*)plan;
   return launch_rows<false>(p, (hipStream_t)stream);
 }
 

@@ -70,7 +70,7 @@ def ragged(lib, **kw):
     (dict(scores=None), 1), (dict(lens=None), 1), (dict(out=None), 1), (dict(stride=0), 1),
     (dict(pt=None), 1), (dict(pts=0), 1), (dict(ps=0), 1), (dict(ps=48), 1),
     (dict(ps=1 << 21), 1), (dict(scores=A4), 2), (dict(stride=66), 2),
-    (dict(plan=A16, plan_bytes=1), 3),
+    (dict(plan=A16, plan_bytes=1), 3), (dict(plan=A4, plan_bytes=1 << 30), 2),
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code

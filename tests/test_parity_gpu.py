@@ -63,11 +63,66 @@ def _edge_rows(k):
     return rows
 
 
+@pytest.mark.parametrize("use_plan", [False, True])
 @pytest.mark.parametrize("mode", ["ragged", "paged"])
 @pytest.mark.parametrize("k", [2048, 1000, 7, 1])
-def test_edge_batch(orc, mode, k):
+def test_edge_batch(orc, mode, k, use_plan):
     p = edge_batch(1000 + k, mode, k, _edge_rows(k), name=f"edge_{mode}_k{k}")
-    check(orc, p, use_plan=(k == 1000))
+    check(orc, p, use_plan=use_plan, with_raw=not use_plan)
+
+
+def _plan_words(plan):
+    return plan.cpu().numpy().view(np.int32)
+
+
+@pytest.mark.parametrize("name", ["paged_long", "paged_mixed"])
+def test_plan_reuse_and_exchange_reset(orc, name):
+    """One plan serves several calls; split rows' exchange areas end zeroed
+    and no segment ever gave up waiting."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload(name)
+    d = gpu_run.to_dev(p)
+    plan = dt.plan(d["lens"], p.k, row_starts=d["starts"])
+    torch.cuda.synchronize()
+    words = _plan_words(plan)
+    n_split, n_items = int(words[12]), int(words[13])
+    assert n_split > 0 and n_items >= 2 * n_split
+    want = expected(orc, p)
+    for _ in range(3):
+        out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+        torch.cuda.synchronize()
+        assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), want, name)
+    words = _plan_words(plan)
+    assert words[14] == 0, "a segment timed out waiting for its row"
+    R = p.num_rows
+    items_word = 64 + 4 * R
+    cap = min(R, 512)
+    xwords = 16704
+    xarea = (items_word + 2 * cap * 17 + 63) // 64 * 64
+    x = words[xarea: xarea + n_split * xwords].reshape(n_split, xwords)
+    # histograms and counters must be zero again; the candidate pairs
+    # (words 4096..8191) are overwritten before they are read
+    assert not x[:, :4096].any(), "level-1 exchange histograms were not left zeroed"
+    assert not x[:, 8192:].any(), "exchange digits / counters were not reset"
+
+
+def test_stale_plan_gives_same_outputs(orc):
+    """A plan built for other lengths still yields exact results."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload("paged_mixed")
+    d = gpu_run.to_dev(p)
+    other = torch.from_numpy(np.roll(p.seq_lens, 7)).to(d["lens"].device)
+    plan = dt.plan(other, p.k)
+    out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+    torch.cuda.synchronize()
+    assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), expected(orc, p), "stale")
+    assert _plan_words(plan)[14] == 0
 
 
 @pytest.mark.parametrize("page_size", [1, 2, 4096])
