@@ -32,6 +32,42 @@ if ROOT not in sys.path:
 METRIC = "DSA top-k rows/s + achieved HBM GB/s (paged decode, L=8K–128K, k=2048)"
 HBM_PEAK_GBPS = 8000.0
 ROTATION_BYTES = 1 << 30
+COPY_CALIBRATION_BYTES = 256 << 20
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_rows_short_kernel_paged_decode.md")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter figures taken from an older build of
+    the kernels no longer describe them."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "row_top_selection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the paged transform kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernels."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        d = json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
 
 
 def algorithmic_bytes(p) -> dict:
@@ -114,21 +150,22 @@ def time_steps(fn, steps: int, warmup: int) -> float:
 
 
 def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
-    """Mean duration of fn(i)'s launches, each bracketed by HIP events on
-    the stream the kernels are launched on (torch's current stream)."""
+    """Mean duration of fn(i)'s launches: `iters` calls back to back between
+    two HIP events recorded on the stream the kernels are launched on
+    (torch's current stream), divided by `iters`."""
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
         fn(warmup + i)
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return 1e3 * a.elapsed_time(b) / iters
 
 
 def cpu_baseline(p, budget_s: float = 12.0) -> dict:
@@ -182,6 +219,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline step and roofline only")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 256 MiB (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the selection shards by rows with no exchange, "
@@ -193,6 +232,14 @@ def main(argv=None):
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_CALIBRATION_BYTES, "launches": 5}), flush=True)
+        return 0
     p = workloads.make_workload("paged_decode")
     r = Runner(p)
     secs = time_steps(r.step, args.steps, args.warmup)
@@ -220,8 +267,9 @@ def main(argv=None):
                    "cold_rotation_copies": r.copies},
         "score_GBps_step": b["score"] * args.steps / secs / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "dsatopk::rows_kernel<paged>", "kernel_us": k_us,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
+                     "kernel": "dsatopk::rows_short_kernel<true>", "kernel_us": k_us,
+                     "kernel_source_hash": kernel_source_hash(),
                      "bytes_per_launch": b, "score_GBps": b["score"] / (k_us * 1e3),
                      "plan_us": plan_us},
     }
