@@ -163,7 +163,7 @@ struct Emit {
       const int32_t e0 = j0 >> page_bits;
       const int32_t n = ((j1 - 1) >> page_bits) - e0 + 1;
       if (n <= kPtCap) {
-        for (int32_t e = threadIdx.x; e < n; e += kBlock) lds[e] = pt[e0 + e];
+        for (int32_t e = threadIdx.x; e < n; e += (int32_t)blockDim.x) lds[e] = pt[e0 + e];
         pt_lds = lds;
         pt_first = e0;
       }
@@ -172,7 +172,8 @@ struct Emit {
 };
 
 // Shared memory of the register path.
-static_assert(kMaxK + kBlock <= kBins, "output stage and its dummies fit the histogram");
+constexpr int kWideBlock = 1024;  // threads per row when rows are too few to fill the chip
+static_assert(kMaxK + kWideBlock <= kBins, "output stage and its dummies fit the histogram");
 
 struct SmemReg {
   uint32_t hist[kBins];       // level-1 histogram; position digits; finally the output stage
@@ -180,7 +181,8 @@ struct SmemReg {
   uint32_t h3[256];           // key bits 11..4
   uint32_t h4[16];            // key bits 3..0
   int32_t pt[kPtCap];         // the row's page-table entries (PAGED)
-  uint32_t wave_cnt[kWaves];  // per wave: selected elements
+  uint32_t wave_cnt[kWideBlock / 64];  // per wave: selected elements
+  uint32_t bcast[4];                   // a bin search's result, when one wave searches
 };
 
 // Shared memory of the streaming path.
@@ -211,7 +213,7 @@ __device__ __forceinline__ float lane_of(const float4& v, int c) {
 
 // Register-resident elements of one workgroup: element (i, c) of thread t is
 // aligned index (i * kBlock + t) * 4 + c.
-template <int NV>
+template <int NV, int BS = kBlock>
 struct RegSrc {
   const uint32_t (&key)[NV][4];
   int32_t origin;  // window position of register element (0, 0) of thread 0
@@ -225,7 +227,7 @@ struct RegSrc {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) f(key[i][c], base + i * kBlock * 4 + c);
+      for (int c = 0; c < 4; ++c) f(key[i][c], base + i * BS * 4 + c);
       // keep the scheduler from hoisting every slot's compare masks (one
       // SGPR pair each) to the top of the pass
       __builtin_amdgcn_sched_barrier(0);
@@ -282,17 +284,39 @@ __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L,
 // used to index the page table.
 // Fully unrolled (k <= kMaxK) with unconditional loads, so the stage and
 // page-table lookups of all iterations are in flight together.
-template <bool kPaged>
+template <bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_t* stage,
                                             int32_t L, int32_t k) {
-  static_assert(kMaxK % kBlock == 0, "whole iterations");
+  static_assert(kMaxK % BS == 0, "whole iterations");
 #pragma unroll
-  for (int i = 0; i < kMaxK / kBlock; ++i) {
-    const int32_t t = i * kBlock + (int32_t)threadIdx.x;
+  for (int i = 0; i < kMaxK / BS; ++i) {
+    const int32_t t = i * BS + (int32_t)threadIdx.x;
     const int32_t j = stage[t];
     const bool ok = (j >= 0) & (j < L);
     const int32_t v = em.value(ok ? j : 0);
     if (t < k) em.out[t] = ok ? v : -1;
+  }
+}
+
+// A bin search whose result every thread needs. With up to 4 waves each
+// wave searches by itself (no barrier); with more, the LDS reads of every
+// wave searching would cost more than a broadcast, so wave 0 searches and
+// the result goes through LDS (one barrier).
+template <int NB, bool kDesc, int BS>
+__device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, SmemReg& sm) {
+  if constexpr (BS <= 256) {
+    return wave_find<NB, kDesc>(hist, need);
+  } else {
+    if (wave_id() == 0) {
+      const BinHit h = wave_find<NB, kDesc>(hist, need);
+      if (lane_id() == 0) {
+        sm.bcast[0] = h.bin;
+        sm.bcast[1] = h.before;
+        sm.bcast[2] = h.cnt;
+      }
+    }
+    __syncthreads();
+    return BinHit{sm.bcast[0], sm.bcast[1], sm.bcast[2]};
   }
 }
 
@@ -302,9 +326,9 @@ __device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_
 // loaded, and each level costs one filtered pass over the registers, one
 // barrier and a 256-bin search. Ties at the k-th key take two position
 // digits in sm.hist (rare). Every wave computes every bin itself.
-template <class Src>
+template <int BS, class Src>
 __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, uint32_t k) {
-  BinHit h = wave_find<kBins, true>(sm.hist, k);
+  BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
   uint32_t need = k - h.before;
   uint32_t prefix = h.bin;  // key bits 31..20
   if (h.cnt == need) return Cut{20, prefix, kAllPos};
@@ -315,7 +339,7 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
     });
   }
   __syncthreads();
-  h = wave_find<256, true>(sm.h2, need);
+  h = group_find<256, true, BS>(sm.h2, need, sm);
   need -= h.before;
   prefix = (prefix << 8) | h.bin;  // bits 31..12
   if (h.cnt == need) return Cut{12, prefix, kAllPos};
@@ -326,7 +350,7 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
     });
   }
   __syncthreads();
-  h = wave_find<256, true>(sm.h3, need);
+  h = group_find<256, true, BS>(sm.h3, need, sm);
   need -= h.before;
   prefix = (prefix << 8) | h.bin;  // bits 31..4
   if (h.cnt == need) return Cut{4, prefix, kAllPos};
@@ -337,7 +361,7 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
     });
   }
   __syncthreads();
-  h = wave_find<16, true>(sm.h4, need);
+  h = group_find<16, true, BS>(sm.h4, need, sm);
   need -= h.before;
   const uint32_t tau = (prefix << 4) | h.bin;
   if (h.cnt == need) return Cut{0, tau, kAllPos};
@@ -346,27 +370,27 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
   // taken: the lowest positions. Window positions are < 2^17: two ascending
   // digits (bits 16..5, then 4..0) find the need-th lowest. The level-1
   // histogram is free (all its readers passed the barriers above).
-  clear_bins<kBins>(sm.hist);
+  clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
   src.for_each([&](uint32_t kk, int32_t j) {
     if (kk == tau) lds_inc(&sm.hist[(uint32_t)j >> 5]);
   });
   __syncthreads();
-  h = wave_find<kBins, false>(sm.hist, need);
+  h = group_find<kBins, false, BS>(sm.hist, need, sm);
   need -= h.before;
   const uint32_t hi = h.bin;
   __syncthreads();
-  clear_bins<32>(sm.hist);
+  clear_bins<32, BS>(sm.hist);
   __syncthreads();
   src.for_each([&](uint32_t kk, int32_t j) {
     if ((kk == tau) & (((uint32_t)j >> 5) == hi)) lds_inc(&sm.hist[(uint32_t)j & 31u]);
   });
   __syncthreads();
-  h = wave_find<32, false>(sm.hist, need);
+  h = group_find<32, false, BS>(sm.hist, need, sm);
   return Cut{0, tau, (int32_t)((hi << 5) | h.bin)};
 }
 
-// Whole span in registers (span <= NV * 4 * kBlock).
+// Whole span in registers (span <= NV * 4 * BS).
 //
 // Every pass over the registers is budgeted in VALU operations per score:
 // at 8 TB/s a CU sees about 3.3 scores per clock against 64 lane-ops per
@@ -379,9 +403,20 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
 // emit order is (wave, lane, register slot): a fixed function of the input.
 // The k selected positions are staged in LDS and mapped and stored in one
 // coalesced pass.
-template <int NV, bool kPaged>
-__device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
-                                                 SmemReg& sm) {
+template <int NV, int BS>
+__device__ __forceinline__ void load_row(const RowView& rv, float4 (&x)[NV]) {
+  const int32_t nvec = (rv.span + 3) >> 2;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int32_t v = i * BS + (int32_t)threadIdx.x;
+    x[i] = v < nvec ? rv.base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// The rest of the register path, once the row's vectors are in x.
+template <int NV, bool kPaged, int BS>
+__device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4 (&x)[NV],
+                                                 int32_t k, Emit<kPaged> em, SmemReg& sm) {
   const int lane = lane_id();
   const int w = wave_id();
   const int32_t t = threadIdx.x;
@@ -389,20 +424,16 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
   const int32_t nvec = (rv.span + 3) >> 2;
   uint32_t key[NV][4];
   {
-    float4 x[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int32_t v = i * kBlock + t;
-      x[i] = v < nvec ? rv.base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     em.stage_table(sm.pt, L);
-    clear_bins<kBins>(sm.hist);
-    sm.h2[t] = 0;  // kBlock == 256 == the size of h2 and h3
-    sm.h3[t] = 0;
+    clear_bins<kBins, BS>(sm.hist);
+    if (t < 256) {
+      sm.h2[t] = 0;
+      sm.h3[t] = 0;
+    }
     if (t < 16) sm.h4[t] = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int32_t v = i * kBlock + t;
+      const int32_t v = i * BS + t;
 #pragma unroll
       for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
       // only the vectors holding the window's first or last columns (or
@@ -423,14 +454,14 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
   // than k in-window keys sit above it).
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    if (i * kBlock + t < nvec) {
+    if (i * BS + t < nvec) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) lds_inc(&sm.hist[key[i][c] >> 20]);
     }
   }
   __syncthreads();
-  const RegSrc<NV> src{key, -rv.rem};
-  const Cut cut = refine_in_registers(src, sm, (uint32_t)k);
+  const RegSrc<NV, BS> src{key, -rv.rem};
+  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
 
   // Selection becomes one compare, key >= thr. Without a partial tie class
   // (the usual case) thr is the cut's lowest key. With one (several
@@ -449,7 +480,7 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
     for (int i = 0; i < NV; ++i) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int32_t j = (i * kBlock + t) * 4 + c - rv.rem;
+        const int32_t j = (i * BS + t) * 4 + c - rv.rem;
         if ((key[i][c] == tau) & (j <= pos)) key[i][c] = tau + 1u;
       }
     }
@@ -470,14 +501,22 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
   // branch-free: unselected elements go to a dummy slot past the k real
   // ones. Then one coalesced pass maps and stores the k outputs.
   int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  const uint32_t dummy = (uint32_t)kMaxK + (uint32_t)t;  // kMaxK + kBlock <= kBins
+  const uint32_t dummy = (uint32_t)kMaxK + (uint32_t)t;  // kMaxK + BS <= kBins
   src.for_each([&](uint32_t kk, int32_t j) {
     const bool sel = kk >= thr;
     stage[(sel & (slot < (uint32_t)k)) ? slot : dummy] = j;
     slot += sel ? 1u : 0u;
   });
   __syncthreads();
-  write_stage(em, stage, L, k);
+  write_stage<kPaged, BS>(em, stage, L, k);
+}
+
+template <int NV, bool kPaged, int BS = kBlock>
+__device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
+                                                 SmemReg& sm) {
+  float4 x[NV];
+  load_row<NV, BS>(rv, x);
+  row_from_vectors<NV, kPaged, BS>(rv, x, k, em, sm);
 }
 
 // Span too long for registers: stream it. Pass 1 builds the level-1
@@ -619,6 +658,25 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const Params p) {
   }
   __shared__ SmemReg sm;
   row_in_registers<kSmallVec>(row_view(p, b, r), p.k, em, sm);
+}
+
+// Same rows with 1024 threads per row (2 float4 per thread), for batches
+// too small to fill the chip: a row's latency, not the rows in flight,
+// sets the time.
+template <bool kPaged>
+__global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
+  RowInfo r;
+  const int64_t b = class_row<kClassShort>(p, r);
+  if (b < 0) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  if (r.L <= p.k) {
+    for (int32_t t = threadIdx.x; t < p.k; t += kWideBlock)
+      em.out[t] = t < r.L ? em.value(t) : -1;
+    return;
+  }
+  __shared__ SmemReg sm;
+  row_in_registers<kSmallVec * kBlock / kWideBlock, kPaged, kWideBlock>(row_view(p, b, r), p.k,
+                                                                         em, sm);
 }
 
 // Spans of 8193 .. 16384 floats, kept in registers.
@@ -1200,6 +1258,10 @@ int check_common(const float* scores, int64_t score_stride, const int32_t* seq_l
   return DSATOPK_OK;
 }
 
+// Up to this many rows, short rows use 1024 threads each: with fewer rows
+// than about two per CU, per-row latency sets the time.
+constexpr int32_t kWideRows = 512;
+
 // Launch the class kernels the score stride allows (a row's span never
 // exceeds score_stride). The plan's row lists are used only when every
 // class is launched: a row whose class changed since planning then still
@@ -1216,7 +1278,10 @@ int launch_rows(Params p, hipStream_t stream) {
     hipLaunchKernelGGL((rows_split_kernel<kPaged>), items, block, 0, stream, p);
   }
   if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, block, 0, stream, p);
-  hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
+  if (p.num_rows <= kWideRows)
+    hipLaunchKernelGGL((rows_wide_kernel<kPaged>), grid, dim3(kWideBlock), 0, stream, p);
+  else
+    hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
   if (mid) hipLaunchKernelGGL((rows_mid_kernel<kPaged>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }

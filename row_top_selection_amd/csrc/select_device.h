@@ -75,14 +75,14 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
-template <int NB>
+template <int NB, int BS = kBlock>
 __device__ __forceinline__ void clear_bins(uint32_t* hist) {
-  if constexpr (NB >= 4 * kBlock) {
+  if constexpr (NB >= 4 * BS) {
     uint4* h4 = reinterpret_cast<uint4*>(hist);
 #pragma unroll
-    for (int i = threadIdx.x; i < NB / 4; i += kBlock) h4[i] = make_uint4(0, 0, 0, 0);
+    for (int i = threadIdx.x; i < NB / 4; i += BS) h4[i] = make_uint4(0, 0, 0, 0);
   } else {
-    for (int i = threadIdx.x; i < NB; i += kBlock) hist[i] = 0;
+    for (int i = threadIdx.x; i < NB; i += BS) hist[i] = 0;
   }
 }
 

@@ -48,6 +48,12 @@ def test_workload(orc, name, use_plan):
     check(orc, p, use_plan, with_raw=not use_plan)
 
 
+def test_many_rows_use_the_narrow_kernel(orc):
+    """More than 512 rows: short rows take the 256-thread kernel."""
+    p = workloads.scaled_decode(1024)
+    check(orc, p, use_plan=False, with_raw=False)
+
+
 def _edge_rows(k):
     rows = []
     for r in range(4):
