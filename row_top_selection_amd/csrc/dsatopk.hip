@@ -132,17 +132,34 @@ __host__ __device__ constexpr int32_t segments_for(int32_t span) {
 template <bool kPaged>
 struct Emit {
   int32_t* out;
-  const int32_t* pt;      // the row's page-table entries (global)
-  const int32_t* pt_lds;  // staged copy of entries pt_first.., or null
-  int32_t pt_first;
+  const int32_t* pt;  // the row's page-table entries (global)
+  int32_t pt_first;   // first entry of the LDS copy, when staged
   int32_t page_bits;
   int32_t offset;
+  bool staged;        // entries pt_first .. sit in the workgroup's LDS table
 
+  __device__ __forceinline__ int32_t map(int32_t j, int32_t page) const {
+    return (int32_t)(((uint32_t)page << page_bits) | ((uint32_t)j & ((1u << page_bits) - 1u)));
+  }
+
+  // The emitted value of window position j, with the page-table entry read
+  // from global memory.
   __device__ __forceinline__ int32_t value(int32_t j) const {
     if constexpr (kPaged) {
-      const int32_t e = j >> page_bits;
-      const int32_t page = pt_lds ? pt_lds[e - pt_first] : pt[e];
-      return (int32_t)(((uint32_t)page << page_bits) | ((uint32_t)j & ((1u << page_bits) - 1u)));
+      return map(j, pt[j >> page_bits]);
+    } else {
+      return j + offset;
+    }
+  }
+
+  // Same, with the entry read from the staged LDS copy `lds`.
+  __device__ __forceinline__ int32_t value_lds(int32_t j, const int32_t* lds) const {
+    if constexpr (kPaged) {
+      // an LDS pointer by type, so that the read is an LDS read even where
+      // the compiler merges this path with the global one
+      const __attribute__((address_space(3))) int32_t* q =
+          (const __attribute__((address_space(3))) int32_t*)lds;
+      return map(j, q[(j >> page_bits) - pt_first]);
     } else {
       return j + offset;
     }
@@ -163,8 +180,8 @@ struct Emit {
       const int32_t e0 = j0 >> page_bits;
       const int32_t n = ((j1 - 1) >> page_bits) - e0 + 1;
       if (n <= kPtCap) {
-        for (int32_t e = threadIdx.x; e < n; e += (int32_t)blockDim.x) lds[e] = pt[e0 + e];
-        pt_lds = lds;
+        for (int32_t e = tix(); e < n; e += (int32_t)blockDim.x) lds[e] = pt[e0 + e];
+        staged = true;
         pt_first = e0;
       }
     }
@@ -173,16 +190,21 @@ struct Emit {
 
 // Shared memory of the register path.
 constexpr int kWideBlock = 1024;  // threads per row when rows are too few to fill the chip
-static_assert(kMaxK + kWideBlock <= kBins, "output stage and its dummies fit the histogram");
+static_assert(kMaxK + kBlock <= kBins, "a split segment's output stage and its dummies fit the histogram");
 
 struct SmemReg {
-  uint32_t hist[kBins];       // level-1 histogram; position digits; finally the output stage
-  uint32_t h2[256];           // key bits 19..12 inside the level-1 bin
-  uint32_t h3[256];           // key bits 11..4
-  uint32_t h4[16];            // key bits 3..0
-  int32_t pt[kPtCap];         // the row's page-table entries (PAGED)
+  uint32_t hist[kBins];                // every histogram of the row's digits; finally the output stage
+  int32_t pt[kPtCap];                  // the row's page-table entries (PAGED)
   uint32_t wave_cnt[kWideBlock / 64];  // per wave: selected elements
   uint32_t bcast[4];                   // a bin search's result, when one wave searches
+};
+
+// The split path also keeps small digit histograms beside its candidate
+// list, which fills the 4096-word array.
+struct SmemSplit : SmemReg {
+  uint32_t h2[256];
+  uint32_t h3[256];
+  uint32_t h4[16];
 };
 
 // Shared memory of the streaming path.
@@ -217,17 +239,20 @@ template <int NV, int BS = kBlock>
 struct RegSrc {
   const uint32_t (&key)[NV][4];
   int32_t origin;  // window position of register element (0, 0) of thread 0
+  int32_t ilast;   // last register slice that holds columns (workgroup-uniform)
 
   // Positions are rebuilt from one opaque base in every pass: the compiler
   // cannot keep NV * 4 position registers alive across passes.
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
-    int32_t base = (int32_t)threadIdx.x * 4 + origin;
+    int32_t base = tix() * 4 + origin;
     asm volatile("" : "+v"(base));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+      if (i <= ilast) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) f(key[i][c], base + i * BS * 4 + c);
+        for (int c = 0; c < 4; ++c) f(key[i][c], base + i * BS * 4 + c);
+      }
       // keep the scheduler from hoisting every slot's compare masks (one
       // SGPR pair each) to the top of the pass
       __builtin_amdgcn_sched_barrier(0);
@@ -261,12 +286,12 @@ struct StreamSrc {
       float4 x[kStreamVec];
 #pragma unroll
       for (int u = 0; u < kStreamVec; ++u) {
-        const int32_t v = v0 + u * kBlock + (int32_t)threadIdx.x;
+        const int32_t v = v0 + u * kBlock + tix();
         x[u] = v < nvec ? rv.base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < kStreamVec; ++u) {
-        const int32_t a0 = (v0 + u * kBlock + (int32_t)threadIdx.x) * 4;
+        const int32_t a0 = (v0 + u * kBlock + tix()) * 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) f(key_at(lane_of(x[u], c), a0 + c, rv), a0 + c - rv.rem);
       }
@@ -276,7 +301,7 @@ struct StreamSrc {
 
 template <bool kPaged>
 __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L, int32_t k) {
-  for (int32_t t = threadIdx.x; t < k; t += kBlock) em.out[t] = t < L ? em.value(t) : -1;
+  for (int32_t t = tix(); t < k; t += kBlock) em.out[t] = t < L ? em.value(t) : -1;
 }
 
 // Final coalesced store of the k staged positions. A position outside
@@ -284,106 +309,114 @@ __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L,
 // used to index the page table.
 // Fully unrolled (k <= kMaxK) with unconditional loads, so the stage and
 // page-table lookups of all iterations are in flight together.
-template <bool kPaged, int BS = kBlock>
-__device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_t* stage,
-                                            int32_t L, int32_t k) {
+template <bool kPaged, int BS, class V>
+__device__ __forceinline__ void write_stage_with(const Emit<kPaged>& em, const int32_t* stage,
+                                                 int32_t L, int32_t k, V value) {
   static_assert(kMaxK % BS == 0, "whole iterations");
 #pragma unroll
   for (int i = 0; i < kMaxK / BS; ++i) {
-    const int32_t t = i * BS + (int32_t)threadIdx.x;
-    const int32_t j = stage[t];
-    const bool ok = (j >= 0) & (j < L);
-    const int32_t v = em.value(ok ? j : 0);
-    if (t < k) em.out[t] = ok ? v : -1;
+    const int32_t t = i * BS + tix();
+    if (t < k) {
+      const int32_t j = stage[t];
+      const bool ok = (uint32_t)j < (uint32_t)L;  // a valid window position
+      const int32_t v = value(ok ? j : 0);
+      em.out[t] = ok ? v : -1;
+    }
   }
 }
 
-// A bin search whose result every thread needs. With up to 4 waves each
-// wave searches by itself (no barrier); with more, the LDS reads of every
-// wave searching would cost more than a broadcast, so wave 0 searches and
-// the result goes through LDS (one barrier).
+// The k staged positions, mapped, to the row's output. `lds_table` is the
+// workgroup's LDS copy of the page table, used when the emit staged it.
+template <bool kPaged, int BS = kBlock>
+__device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_t* stage,
+                                            int32_t L, int32_t k, const int32_t* lds_table) {
+  if (kPaged && em.staged)
+    write_stage_with<kPaged, BS>(em, stage, L, k,
+                                 [&](int32_t j) { return em.value_lds(j, lds_table); });
+  else
+    write_stage_with<kPaged, BS>(em, stage, L, k, [&](int32_t j) { return em.value(j); });
+}
+
+// A bin search whose result every thread needs: wave 0 searches and the
+// result goes through LDS (one barrier). Several workgroups share a CU, so
+// the issue slots of the idle waves are not lost, while a search by every
+// wave would multiply its VALU work by the wave count.
 template <int NB, bool kDesc, int BS>
 __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, SmemReg& sm) {
-  if constexpr (BS <= 256) {
-    return wave_find<NB, kDesc>(hist, need);
-  } else {
-    if (wave_id() == 0) {
-      const BinHit h = wave_find<NB, kDesc>(hist, need);
-      if (lane_id() == 0) {
-        sm.bcast[0] = h.bin;
-        sm.bcast[1] = h.before;
-        sm.bcast[2] = h.cnt;
-      }
+  if (wave_id() == 0) {
+    const BinHit h = wave_find<NB, kDesc>(hist, need);
+    if (lane_id() == 0) {
+      sm.bcast[0] = h.bin;
+      sm.bcast[1] = h.before;
+      sm.bcast[2] = h.cnt;
     }
-    __syncthreads();
-    return BinHit{sm.bcast[0], sm.bcast[1], sm.bcast[2]};
   }
+  __syncthreads();
+  return BinHit{(uint32_t)__builtin_amdgcn_readfirstlane(sm.bcast[0]),
+                (uint32_t)__builtin_amdgcn_readfirstlane(sm.bcast[1]),
+                (uint32_t)__builtin_amdgcn_readfirstlane(sm.bcast[2])};
 }
 
 // The cut of a register-resident row. Level 1 (key bits 31..20) was
-// histogrammed into sm.hist by the caller. The remaining key digits are 8,
-// 8 and 4 bits wide: their histograms are small, cleared when the row was
-// loaded, and each level costs one filtered pass over the registers, one
-// barrier and a 256-bin search. Ties at the k-th key take two position
-// digits in sm.hist (rare). Every wave computes every bin itself.
+// histogrammed into sm.hist by the caller. Level 2 takes the next 12 bits
+// (19..8) in the same array, cleared once its level-1 search is done;
+// level 3 the last 8 bits. Each level costs one filtered pass over the
+// registers and a search by wave 0. Ties at the k-th key take two position
+// digits (rare).
 template <int BS, class Src>
 __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, uint32_t k) {
   BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
   uint32_t need = k - h.before;
   uint32_t prefix = h.bin;  // key bits 31..20
   if (h.cnt == need) return Cut{20, prefix, kAllPos};
+  // every wave is past the search's barrier: the level-1 counts are dead
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
   {
     const uint32_t p = prefix;
+    const uint32_t one = opaque_one();
     src.for_each([&](uint32_t kk, int32_t) {
-      if ((kk >> 20) == p) lds_inc(&sm.h2[(kk >> 12) & 0xffu]);
+      if ((kk >> 20) == p) lds_add(&sm.hist[(kk >> 8) & 0xfffu], one);
     });
   }
   __syncthreads();
-  h = group_find<256, true, BS>(sm.h2, need, sm);
+  h = group_find<kBins, true, BS>(sm.hist, need, sm);
   need -= h.before;
-  prefix = (prefix << 8) | h.bin;  // bits 31..12
-  if (h.cnt == need) return Cut{12, prefix, kAllPos};
+  prefix = (prefix << 12) | h.bin;  // bits 31..8
+  if (h.cnt == need) return Cut{8, prefix, kAllPos};
+  clear_bins<256, BS>(sm.hist);
+  __syncthreads();
   {
     const uint32_t p = prefix;
+    const uint32_t one = opaque_one();
     src.for_each([&](uint32_t kk, int32_t) {
-      if ((kk >> 12) == p) lds_inc(&sm.h3[(kk >> 4) & 0xffu]);
+      if ((kk >> 8) == p) lds_add(&sm.hist[kk & 0xffu], one);
     });
   }
   __syncthreads();
-  h = group_find<256, true, BS>(sm.h3, need, sm);
+  h = group_find<256, true, BS>(sm.hist, need, sm);
   need -= h.before;
-  prefix = (prefix << 8) | h.bin;  // bits 31..4
-  if (h.cnt == need) return Cut{4, prefix, kAllPos};
-  {
-    const uint32_t p = prefix;
-    src.for_each([&](uint32_t kk, int32_t) {
-      if ((kk >> 4) == p) lds_inc(&sm.h4[kk & 0xfu]);
-    });
-  }
-  __syncthreads();
-  h = group_find<16, true, BS>(sm.h4, need, sm);
-  need -= h.before;
-  const uint32_t tau = (prefix << 4) | h.bin;
+  const uint32_t tau = (prefix << 8) | h.bin;
   if (h.cnt == need) return Cut{0, tau, kAllPos};
 
   // Several elements hold exactly the key tau and only `need` of them are
   // taken: the lowest positions. Window positions are < 2^17: two ascending
-  // digits (bits 16..5, then 4..0) find the need-th lowest. The level-1
-  // histogram is free (all its readers passed the barriers above).
+  // digits (bits 16..5, then 4..0) find the need-th lowest. Columns before
+  // the window have negative positions and key 0; they are left out so that
+  // every bin index stays inside the histogram.
   clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
   src.for_each([&](uint32_t kk, int32_t j) {
-    if (kk == tau) lds_inc(&sm.hist[(uint32_t)j >> 5]);
+    if ((kk == tau) & (j >= 0)) lds_inc(&sm.hist[(uint32_t)j >> 5]);
   });
   __syncthreads();
   h = group_find<kBins, false, BS>(sm.hist, need, sm);
   need -= h.before;
   const uint32_t hi = h.bin;
-  __syncthreads();
   clear_bins<32, BS>(sm.hist);
   __syncthreads();
   src.for_each([&](uint32_t kk, int32_t j) {
-    if ((kk == tau) & (((uint32_t)j >> 5) == hi)) lds_inc(&sm.hist[(uint32_t)j & 31u]);
+    if ((kk == tau) & (j >= 0) & (((uint32_t)j >> 5) == hi)) lds_inc(&sm.hist[(uint32_t)j & 31u]);
   });
   __syncthreads();
   h = group_find<32, false, BS>(sm.hist, need, sm);
@@ -403,119 +436,189 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, 
 // emit order is (wave, lane, register slot): a fixed function of the input.
 // The k selected positions are staged in LDS and mapped and stored in one
 // coalesced pass.
-template <int NV, int BS>
-__device__ __forceinline__ void load_row(const RowView& rv, float4 (&x)[NV]) {
-  const int32_t nvec = (rv.span + 3) >> 2;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int32_t v = i * BS + (int32_t)threadIdx.x;
-    x[i] = v < nvec ? rv.base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+// Cache policy of the score loads: non-temporal. Scores are read once;
+// streaming them past the caches leaves L2 and the Infinity Cache to the
+// output writes, which raises the combined read+write rate of a launch by
+// about a fifth on MI355X.
+constexpr int kStreamingLoad = 2;
+
+// A raw buffer over the row's nvec aligned vectors: its loads take the
+// slice offset from a scalar register, and the hardware returns zeros for
+// vectors past the end instead of reading them, so no load needs a compare.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const float4* base4, int32_t nvec) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base4);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  // dword 3: 32-bit data format, the setting of untyped loads on gfx9-class GPUs
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
+                                           __builtin_amdgcn_readfirstlane(nvec * 16), 0x00020000);
 }
 
-// The rest of the register path, once the row's vectors are in x.
+// Vector v0 + i * BS + t of the row into x[i] (zeros past the row's last vector).
+template <int NV, int BS>
+__device__ __forceinline__ void load_vectors(const float4* base4, int32_t nvec, int32_t v0,
+                                             float4 (&x)[NV]) {
+  const __amdgpu_buffer_rsrc_t r = row_buffer(base4, nvec);
+  const int32_t off = (v0 + tix()) * 16;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    x[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, i * BS * 16,
+                                                                            kStreamingLoad));
+}
+
+template <int NV, int BS>
+__device__ __forceinline__ void load_row(const RowView& rv, float4 (&x)[NV]) {
+  load_vectors<NV, BS>(rv.base4, (rv.span + 3) >> 2, 0, x);
+}
+
+// Positions of the elements `sel` takes, into stage[0 ..) in register
+// order: each thread counts its own, a scan over the workgroup gives its
+// first slot, and a second pass writes them. Without kGuard the caller
+// guarantees that at most k elements are taken.
+template <int BS, bool kGuard, class Src, class Sel>
+__device__ __forceinline__ void stage_selected(const Src& src, Sel sel, uint32_t k,
+                                               int32_t* stage, SmemReg& sm) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  uint32_t mine = 0;
+  src.for_each([&](uint32_t kk, int32_t j) { mine = add_lane_bit(mine, __ballot(sel(kk, j))); });
+  const uint32_t incl = wave_inclusive_sum(mine);
+  if (lane == 63) sm.wave_cnt[w] = incl;
+  __syncthreads();
+  uint32_t slot = incl - mine;
+  for (int v = 0; v < w; ++v) slot += sm.wave_cnt[v];
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = sel(kk, j);
+    const uint64_t m = __ballot(s);
+    if (kGuard ? (s & (slot < k)) : s) stage[slot] = j;
+    slot = add_lane_bit(slot, m);
+  });
+}
+
+// The rest of the register path, once the row's vectors are in x (and the
+// caller has staged the page table, if it stages it).
 template <int NV, bool kPaged, int BS>
 __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4 (&x)[NV],
                                                  int32_t k, Emit<kPaged> em, SmemReg& sm) {
-  const int lane = lane_id();
-  const int w = wave_id();
-  const int32_t t = threadIdx.x;
+  const int32_t t = tix();
   const int32_t L = rv.span - rv.rem;
-  const int32_t nvec = (rv.span + 3) >> 2;
+  // Register slices 0 .. ilast hold the span's vectors; later slices hold
+  // nothing of the row, and every pass skips them.
+  const int32_t ilast = __builtin_amdgcn_readfirstlane((((rv.span + 3) >> 2) - 1) / BS);
   uint32_t key[NV][4];
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
+  // Slice by slice as its loads land: keys, then the level-1 histogram.
+  // Columns outside the window get key 0, below every float's key except
+  // the all-ones NaN: in the first vector the columns before the window
+  // start, and in slice ilast every column at or past the span. All other
+  // columns of slices 0 .. ilast lie inside the window. The outside columns
+  // count in bin 0 like in every later pass, so the counts of all passes
+  // agree.
   {
-    em.stage_table(sm.pt, L);
-    clear_bins<kBins, BS>(sm.hist);
-    if (t < 256) {
-      sm.h2[t] = 0;
-      sm.h3[t] = 0;
-    }
-    if (t < 16) sm.h4[t] = 0;
+    const uint32_t one = opaque_one();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int32_t v = i * BS + t;
+      if (i <= ilast) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
-      // only the vectors holding the window's first or last columns (or
-      // none of it) carry columns outside the window
-      if ((v == 0) | (v * 4 + 4 > rv.span)) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int32_t a = v * 4 + c;
-          if ((a < rv.rem) | (a >= rv.span)) key[i][c] = 0;
+        for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
+        if (i == 0 && t == 0) {
+          if (rv.rem > 0) key[0][0] = 0u;
+          if (rv.rem > 1) key[0][1] = 0u;
+          if (rv.rem > 2) key[0][2] = 0u;
         }
+        if (i == ilast) {
+          const int32_t a = 4 * (i * BS + t);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (a + c >= rv.span) key[i][c] = 0u;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
       }
     }
   }
   __syncthreads();
-  // Level-1 histogram. Vectors past the span are skipped; the few columns
-  // outside the window inside the edge vectors land in bin 0, which the
-  // descending scan never reaches (bin 0 holds no float's key, and more
-  // than k in-window keys sit above it).
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (i * BS + t < nvec) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lds_inc(&sm.hist[key[i][c] >> 20]);
-    }
-  }
-  __syncthreads();
-  const RegSrc<NV, BS> src{key, -rv.rem};
+  const RegSrc<NV, BS> src{key, -rv.rem, ilast};
   const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
 
-  // Selection becomes one compare, key >= thr. Without a partial tie class
-  // (the usual case) thr is the cut's lowest key. With one (several
-  // elements hold exactly the k-th key tau, and only those at positions
-  // <= pos are taken), a rare extra pass raises the taken tied keys to
-  // tau + 1 and thr = tau + 1. (tau + 1 cannot wrap: no float's key is
-  // all ones.)
-  uint32_t thr;
+  // Stage the selected positions in LDS (the histogram's space, free now),
+  // then one coalesced pass maps and stores the k outputs. Without a
+  // partial tie class (the usual case) the selection is key >= thr, and the
+  // cut's counts make that at most k elements. With one (several elements
+  // hold exactly the k-th key tau and only those at positions <= pos are
+  // taken) the rare second form applies, with a guard on the slot.
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
   if (cut.pos == kAllPos) {
     const uint32_t lo = cut.prefix << cut.shift;
-    thr = lo ? lo : 1u;
+    const uint32_t thr = lo ? lo : 1u;
+    stage_selected<BS, false>(
+        src, [thr](uint32_t kk, int32_t) { return kk >= thr; }, (uint32_t)k, stage, sm);
   } else {
     const uint32_t tau = cut.prefix;
     const int32_t pos = cut.pos;
+    stage_selected<BS, true>(
+        src,
+        [tau, pos](uint32_t kk, int32_t j) {
+          return (kk != 0u) & ((kk > tau) | ((kk == tau) & (j <= pos)));
+        },
+        (uint32_t)k, stage, sm);
+  }
+  __syncthreads();
+  write_stage<kPaged, BS>(em, stage, L, k, sm.pt);
+}
+
+// The page-table entries of window [0, L) into registers (entry e in
+// v[e / BS] of thread e % BS) when they fit the LDS table, then into the
+// table. The loads are issued before the row's score loads, so the wait for
+// them before the LDS store does not also wait for the scores.
+template <int BS>
+constexpr int table_per_thread() {
+  return (kPtCap + BS - 1) / BS;
+}
+
+template <bool kPaged, int BS>
+__device__ __forceinline__ void load_table(const Emit<kPaged>& em, int32_t L,
+                                           int32_t (&v)[table_per_thread<BS>()]) {
+  if constexpr (kPaged) {
+    const int32_t n = L > 0 ? ((L - 1) >> em.page_bits) + 1 : 0;
+    if (n <= kPtCap) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int32_t j = (i * BS + t) * 4 + c - rv.rem;
-        if ((key[i][c] == tau) & (j <= pos)) key[i][c] = tau + 1u;
+      for (int q = 0; q < table_per_thread<BS>(); ++q) {
+        const int32_t e = q * BS + tix();
+        v[q] = e < n ? em.pt[e] : 0;
       }
     }
-    thr = tau + 1u;
   }
+}
 
-  // Each thread's output count, then its first output slot: lane l of wave
-  // w writes after all lower waves and after lanes < l of its wave.
-  uint32_t mine = 0;
-  src.for_each([&](uint32_t kk, int32_t) { mine += (kk >= thr) ? 1u : 0u; });
-  const uint32_t mine_incl = wave_inclusive_sum(mine);
-  if (lane == 63) sm.wave_cnt[w] = mine_incl;
-  __syncthreads();
-  uint32_t slot = mine_incl - mine;
-  for (int v = 0; v < w; ++v) slot += sm.wave_cnt[v];
-
-  // Stage the selected positions in LDS (the histogram's space, free now),
-  // branch-free: unselected elements go to a dummy slot past the k real
-  // ones. Then one coalesced pass maps and stores the k outputs.
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  const uint32_t dummy = (uint32_t)kMaxK + (uint32_t)t;  // kMaxK + BS <= kBins
-  src.for_each([&](uint32_t kk, int32_t j) {
-    const bool sel = kk >= thr;
-    stage[(sel & (slot < (uint32_t)k)) ? slot : dummy] = j;
-    slot += sel ? 1u : 0u;
-  });
-  __syncthreads();
-  write_stage<kPaged, BS>(em, stage, L, k);
+template <bool kPaged, int BS>
+__device__ __forceinline__ void store_table(Emit<kPaged>& em, int32_t* lds, int32_t L,
+                                            const int32_t (&v)[table_per_thread<BS>()]) {
+  if constexpr (kPaged) {
+    const int32_t n = L > 0 ? ((L - 1) >> em.page_bits) + 1 : 0;
+    if (n <= kPtCap) {
+#pragma unroll
+      for (int q = 0; q < table_per_thread<BS>(); ++q) {
+        const int32_t e = q * BS + tix();
+        if (e < n) lds[e] = v[q];
+      }
+      em.staged = true;
+      em.pt_first = 0;
+    }
+  }
 }
 
 template <int NV, bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
                                                  SmemReg& sm) {
+  const int32_t L = rv.span - rv.rem;
+  int32_t tv[table_per_thread<BS>()];
+  load_table<kPaged, BS>(em, L, tv);
   float4 x[NV];
   load_row<NV, BS>(rv, x);
+  store_table<kPaged, BS>(em, sm.pt, L, tv);
   row_from_vectors<NV, kPaged, BS>(rv, x, k, em, sm);
 }
 
@@ -530,7 +633,7 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
   const StreamSrc src{rv};
   const int32_t L = rv.span - rv.rem;
   clear_bins<kBins>(sm.hist);
-  if (threadIdx.x == 0) {
+  if (tix() == 0) {
     sm.nstage = 0;
     sm.ncand = 0;
   }
@@ -570,7 +673,7 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
     });
   }
   __syncthreads();
-  write_stage(em, sm.stage, L, k);
+  write_stage(em, sm.stage, L, k, nullptr);
 }
 
 template <bool kPaged>
@@ -578,7 +681,7 @@ __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b) {
   Emit<kPaged> em;
   em.out = p.out + b * p.k;
   em.page_bits = p.page_bits;
-  em.pt_lds = nullptr;
+  em.staged = false;
   em.pt_first = 0;
   if constexpr (kPaged) {
     em.pt = p.page_table + b * p.pt_stride;
@@ -632,17 +735,24 @@ __device__ __forceinline__ bool plan_ok(const Params& p) {
 }
 
 template <int kClass>
-__device__ __forceinline__ int64_t class_row(const Params& p, RowInfo& r) {
-  int64_t b = blockIdx.x;
-  if (plan_ok(p)) {
-    const uint32_t i = (uint32_t)p.plan[kPlanWordOffset + kClass] + blockIdx.x;
-    if ((int32_t)blockIdx.x >= p.plan[kPlanWordCount + kClass] || i >= (uint32_t)p.num_rows)
-      return -1;
-    b = p.plan[kPlanHeaderWords + i];
+__device__ __forceinline__ int64_t class_row_at(const Params& p, bool planned, int32_t i,
+                                                RowInfo& r) {
+  int64_t b = i;
+  if (planned) {
+    const uint32_t li = (uint32_t)p.plan[kPlanWordOffset + kClass] + (uint32_t)i;
+    if (i >= p.plan[kPlanWordCount + kClass] || li >= (uint32_t)p.num_rows) return -1;
+    b = p.plan[kPlanHeaderWords + li];
     if ((uint64_t)b >= (uint64_t)p.num_rows) return -1;
+  } else if (i >= p.num_rows) {
+    return -1;
   }
   r = row_info(p.seq_lens, p.row_starts, p.k, b);
   return r.cls == kClass ? b : -1;
+}
+
+template <int kClass>
+__device__ __forceinline__ int64_t class_row(const Params& p, RowInfo& r) {
+  return class_row_at<kClass>(p, plan_ok(p), (int32_t)blockIdx.x, r);
 }
 
 // Trivial rows and spans <= 8192 floats, kept in registers.
@@ -670,7 +780,7 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
   if (b < 0) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
-    for (int32_t t = threadIdx.x; t < p.k; t += kWideBlock)
+    for (int32_t t = tix(); t < p.k; t += kWideBlock)
       em.out[t] = t < r.L ? em.value(t) : -1;
     return;
   }
@@ -762,7 +872,7 @@ struct SplitSync {
   __device__ __forceinline__ bool arrive(uint32_t round) const {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's atomics completed
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tix() == 0) {
       const uint32_t prev =
           __hip_atomic_fetch_add(&x[kXArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_word[0] = prev == (uint32_t)S * round - 1u;
@@ -773,7 +883,7 @@ struct SplitSync {
 
   // Last arriver: make `payload` the result of `round`.
   __device__ __forceinline__ void publish(uint32_t round, uint64_t payload) const {
-    if (threadIdx.x == 0) {
+    if (tix() == 0) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __hip_atomic_store(reinterpret_cast<uint64_t*>(x + kXFlag), pack_round(round, payload),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -783,7 +893,7 @@ struct SplitSync {
   // Everyone: the published result of `round` (the last arriver passes
   // `mine`, which it just published).
   __device__ __forceinline__ uint64_t result(uint32_t round, bool last, uint64_t mine) const {
-    if (threadIdx.x == 0) {
+    if (tix() == 0) {
       uint64_t w = mine;
       if (!last) {
         const uint64_t* f = reinterpret_cast<const uint64_t*>(x + kXFlag);
@@ -815,7 +925,7 @@ template <int NB, bool kDesc>
 __device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
                                                   uint32_t round, uint32_t need,
                                                   const SplitSync& sy) {
-  const int32_t t = threadIdx.x;
+  const int32_t t = tix();
   __syncthreads();  // local histogram complete
   for (int32_t i = t; i < NB; i += kBlock) {
     const uint32_t v = lds_hist[i];
@@ -840,7 +950,7 @@ __device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* 
 // (tau, pos): select key > tau, or key == tau and position <= pos.
 __device__ __forceinline__ uint64_t resolve_pairs_wave(const uint2* cand, uint32_t n,
                                                        uint32_t prefix, uint32_t need,
-                                                       SmemReg& sm) {
+                                                       SmemSplit& sm) {
   const int lane = lane_id();
   uint32_t pbits = 12;  // key bits fixed so far (from the top)
   const uint32_t key_shift[3] = {12, 4, 0};
@@ -914,9 +1024,9 @@ __device__ __forceinline__ uint64_t resolve_pairs_wave(const uint2* cand, uint32
 template <bool kPaged>
 __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b, const RowInfo& r,
                                                      int32_t seg, int32_t S, uint32_t* x,
-                                                     SmemReg& sm, uint32_t* s_word) {
+                                                     SmemSplit& sm, uint32_t* s_word) {
   constexpr int NV = kSmallVec;
-  const int32_t t = threadIdx.x;
+  const int32_t t = tix();
   const int lane = lane_id();
   const int w = wave_id();
   const uint32_t k = (uint32_t)p.k;
@@ -929,11 +1039,7 @@ __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b,
   uint32_t key[NV][4];
   {
     float4 xv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int32_t v = v0 + i * kBlock + t;
-      xv[i] = v < nvec ? base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    load_vectors<NV, kBlock>(base4, nvec, v0, xv);
     const int32_t j0 = v0 * 4 - rem;
     const int32_t j1 = j0 + kSegLen < r.L ? j0 + kSegLen : r.L;
     em.stage_table_range(sm.pt, j0, j1);
@@ -952,7 +1058,7 @@ __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b,
       }
     }
   }
-  const RegSrc<NV> src{key, v0 * 4 - rem};
+  const RegSrc<NV> src{key, v0 * 4 - rem, NV - 1};
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -1107,11 +1213,17 @@ __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b,
     s_word[0] = __hip_atomic_fetch_add(&x[kXOut], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t base = s_word[0];
-  for (uint32_t i = t; i < total; i += kBlock) {
-    const int32_t j = stage[i];
-    const bool ok = (j >= 0) & (j < r.L) & (base + i < k);
-    if (ok) em.out[base + i] = em.value(j);
-  }
+  auto emit = [&](auto value) {
+    for (uint32_t i = t; i < total; i += kBlock) {
+      const int32_t j = stage[i];
+      const bool ok = ((uint32_t)j < (uint32_t)r.L) & (base + i < k);
+      if (ok) em.out[base + i] = value(j);
+    }
+  };
+  if (kPaged && em.staged)
+    emit([&](int32_t j) { return em.value_lds(j, sm.pt); });
+  else
+    emit([&](int32_t j) { return em.value(j); });
   __syncthreads();  // s_word is reused below
   if (t == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1151,7 +1263,7 @@ __global__ __launch_bounds__(kBlock) void rows_split_kernel(const Params p) {
   if (seg < 0 || seg >= S) return;
   const int32_t slot = p.plan[plan_slot_word(R) + b];
   uint32_t* x = reinterpret_cast<uint32_t*>(p.plan + plan_xarea_word(R) + (int64_t)slot * kXWords);
-  __shared__ SmemReg sm;
+  __shared__ SmemSplit sm;
   __shared__ uint32_t s_word[2];
   segment_in_registers<kPaged>(p, b, r, seg, S, x, sm, s_word);
 }
@@ -1167,11 +1279,11 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   __shared__ uint32_t fill[3];
   __shared__ uint32_t n_split;
   __shared__ uint32_t n_items;
-  if (threadIdx.x < 3) {
-    count[threadIdx.x] = 0;
-    fill[threadIdx.x] = 0;
+  if (tix() < 3) {
+    count[tix()] = 0;
+    fill[tix()] = 0;
   }
-  if (threadIdx.x == 0) {
+  if (tix() == 0) {
     n_split = 0;
     n_items = 0;
   }
@@ -1181,7 +1293,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   int32_t* slot = plan + plan_slot_word(num_rows);
   int32_t* items = plan + plan_items_word(num_rows);
   const uint32_t cap = (uint32_t)plan_split_cap(num_rows);
-  for (int32_t b = threadIdx.x; b < num_rows; b += kPlanBlock) {
+  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const RowInfo r = row_info(seq_lens, row_starts, k, b);
     cls[b] = r.cls;
     atomicAdd(&count[r.cls], 1u);
@@ -1205,11 +1317,11 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   __syncthreads();
   const uint32_t off[3] = {0u, count[0], count[0] + count[1]};
   int32_t* list = plan + kPlanHeaderWords;
-  for (int32_t b = threadIdx.x; b < num_rows; b += kPlanBlock) {
+  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const int32_t c = cls[b];
     list[off[c] + atomicAdd(&fill[c], 1u)] = b;
   }
-  if (threadIdx.x == 0) {
+  if (tix() == 0) {
     plan[kPlanWordMagic] = kPlanMagic;
     plan[kPlanWordRows] = num_rows;
     plan[kPlanWordK] = k;
@@ -1228,7 +1340,7 @@ __global__ __launch_bounds__(kBlock) void plan_clear_kernel(int32_t num_rows, in
   const int32_t q = blockIdx.x;
   if (q >= plan[kPlanWordSplit]) return;
   int32_t* x = plan + plan_xarea_word(num_rows) + (int64_t)q * kXWords;
-  for (int32_t i = threadIdx.x; i < kXWords; i += kBlock) x[i] = 0;
+  for (int32_t i = tix(); i < kXWords; i += kBlock) x[i] = 0;
 }
 
 }  // namespace dsatopk
@@ -1278,10 +1390,11 @@ int launch_rows(Params p, hipStream_t stream) {
     hipLaunchKernelGGL((rows_split_kernel<kPaged>), items, block, 0, stream, p);
   }
   if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, block, 0, stream, p);
-  if (p.num_rows <= kWideRows)
+  if (p.num_rows <= kWideRows) {
     hipLaunchKernelGGL((rows_wide_kernel<kPaged>), grid, dim3(kWideBlock), 0, stream, p);
-  else
+  } else {
     hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
+  }
   if (mid) hipLaunchKernelGGL((rows_mid_kernel<kPaged>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }

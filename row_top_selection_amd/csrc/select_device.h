@@ -37,19 +37,57 @@ constexpr int kAllPos = 0x7fffffff;  // "every tied position" in a cut
 // ~u (so -0.0 -> 0x7fffffff); non-negative floats map to (u | 2^31) - 1
 // (so +0.0 -> 0x7fffffff too; the shift by one keeps the order). Key 0 is
 // reserved for "not in the window": no float maps to it except the
-// all-ones negative NaN, and NaNs are outside the contract. Four VALU ops.
+// all-ones negative NaN, and NaNs are outside the contract. Written as
+// (u ^ s) + (~s & 0x7fffffff) with s the sign mask: for a negative float
+// that is ~u + 0, for a non-negative one u + 2^31 - 1, the same key; it
+// compiles to three VALU ops (shift, bit select, xor-add).
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t s = (uint32_t)((int32_t)u >> 31);  // all ones if negative
-  return (u ^ (s | 0x80000000u)) + ~s;
+  return (u ^ s) + (~s & 0x7fffffffu);
 }
 
 __device__ __forceinline__ void lds_inc(uint32_t* p) {
   __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Adds v to an LDS counter. With v from opaque_one() the constant stays in
+// one VGPR for a whole pass; a literal 1 is rebuilt in every exec-masked
+// block of a filtered pass.
+__device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ uint32_t opaque_one() {
+  uint32_t one = 1u;
+  asm volatile("" : "+v"(one));
+  return one;
+}
+
+// x + (this lane's bit of the lane mask m), as one add-with-carry that
+// takes the mask (a compare's result) as its carry-in.
+__device__ __forceinline__ uint32_t add_lane_bit(uint32_t x, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, 0, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(x), "s"(m));
+  return r;
+}
+
+// threadIdx.x, opaque to the optimizer: values derived from it are rebuilt
+// where they are used instead of being hoisted out of a row loop and held
+// in VGPRs for the whole kernel (which cost the persistent kernel a third
+// of its occupancy).
+__device__ __forceinline__ int tix() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ int lane_id() { return tix() & 63; }
+// The wave's index in the workgroup, as a scalar (the same for all lanes).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(tix() >> 6);
+}
 
 // Orders this wave's LDS accesses: everything issued before is complete and
 // visible to every lane of the wave afterwards.
@@ -80,9 +118,9 @@ __device__ __forceinline__ void clear_bins(uint32_t* hist) {
   if constexpr (NB >= 4 * BS) {
     uint4* h4 = reinterpret_cast<uint4*>(hist);
 #pragma unroll
-    for (int i = threadIdx.x; i < NB / 4; i += BS) h4[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tix(); i < NB / 4; i += BS) h4[i] = make_uint4(0, 0, 0, 0);
   } else {
-    for (int i = threadIdx.x; i < NB; i += BS) hist[i] = 0;
+    for (int i = tix(); i < NB; i += BS) hist[i] = 0;
   }
 }
 

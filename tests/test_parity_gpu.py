@@ -54,6 +54,18 @@ def test_many_rows_use_the_narrow_kernel(orc):
     check(orc, p, use_plan=False, with_raw=False)
 
 
+@pytest.mark.parametrize("use_plan", [False, True])
+@pytest.mark.parametrize("mode", ["paged", "ragged"])
+def test_large_short_batch(orc, mode, use_plan):
+    """4096 short rows with mixed lengths and window offsets, trivial rows
+    among them, and fp16 ties: many workgroups of the short-row kernel."""
+    p = workloads.short_mix(4096, mode)
+    assert (p.seq_lens <= p.k).any() and (p.seq_lens > p.k).any()
+    got = check(orc, p, use_plan, with_raw=False)
+    again, _ = gpu_run.run(p, gpu_run.to_dev(p), use_plan=use_plan)
+    assert np.array_equal(got, again), "register rows are byte-deterministic"
+
+
 def _edge_rows(k):
     rows = []
     for r in range(4):

@@ -28,5 +28,6 @@ from .configs import (  # noqa: F401
     make_workload,
     scaled_decode,
     scaled_long,
+    short_mix,
     random_page_tables,
 )

@@ -158,6 +158,34 @@ def scaled_decode(rows: int, seed: Optional[int] = None) -> Problem:
     return p
 
 
+def short_mix(rows: int, mode: str, seed: Optional[int] = None) -> Problem:
+    """Many rows of the short class (span <= 8192 columns) with mixed shapes:
+    window starts at column 0..3 (every residue mod 4); even rows log-uniform
+    lengths in [1, 8192 - start] (mostly trivial, L <= k), odd rows uniform in
+    [1001, 8192 - start]; k = 1000, N(0,1)
+    scores of which every 16th row is rounded to fp16 (ties at the cut).
+    PAGED: page size 64, 128 table entries per row from 4096 pages; RAGGED:
+    random output offsets below 2^20."""
+    if seed is None:
+        seed = BASE_SEED + 105
+    rng = np.random.default_rng(seed)
+    stride = 8192 + 4
+    starts = rng.integers(0, 4, size=rows).astype(np.int32)
+    u = rng.random(rows)
+    logu = np.floor(np.exp(u * np.log(8193 - starts)))
+    unif = 1001 + np.floor(u * (8192 - starts - 1000))
+    seq_lens = np.where(np.arange(rows) % 2 == 0, logu, unif)
+    seq_lens = np.clip(seq_lens, 1, 8192 - starts).astype(np.int32)
+    scores = _normal(rng, (rows, stride))
+    scores[::16] = scores[::16].astype(np.float16).astype(np.float32)
+    name = f"short_mix_{mode}_x{rows}"
+    if mode == "paged":
+        pt = random_page_tables(rng, rows, 128, 4096)
+        return Problem(name, "paged", 1000, scores, seq_lens, row_starts=starts, page_table=pt)
+    offs = rng.integers(0, 1 << 20, size=rows).astype(np.int32)
+    return Problem(name, "ragged", 1000, scores, seq_lens, row_starts=starts, out_offsets=offs)
+
+
 def scaled_long(rows: int, seed: Optional[int] = None) -> Problem:
     """``paged_long``'s per-row shape with ``rows`` rows (sustained-rate runs)."""
     if seed is None:
