@@ -4,7 +4,10 @@ Step: one pass of the whole path over one batch: dsatopk_plan followed by
 dsatopk_paged on the ``paged_decode`` workload (128 rows x 8192 fp32 scores,
 k = 2048, page size 64, random page tables). Inputs are resident in HBM;
 every step reads a different copy of the scores from a rotation of at least
-1 GiB so that score reads miss the 256 MB Infinity Cache.
+1 GiB so that score reads miss the 256 MB Infinity Cache. The W warmup and K
+timed steps are each captured once into a HIP graph and replayed, the way a
+serving loop issues them; the same steps issued call by call from Python are
+reported beside it ("eager"), where host launch overhead dominates.
 
 Also reported (same JSON line):
   roofline      the paged transform kernel: algorithmic bytes per launch
@@ -149,6 +152,34 @@ def time_steps(fn, steps: int, warmup: int) -> float:
     return time.perf_counter() - t0
 
 
+def capture_steps(fn, start: int, n: int):
+    """A HIP graph of n consecutive steps fn(start), fn(start + 1), ... (the
+    library's calls only launch kernels, so they capture as they are)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(start + i)
+    return g
+
+
+def time_graph_steps(fn, steps: int, warmup: int) -> float:
+    """Seconds for `steps` steps replayed from one captured graph, after a
+    replay of `warmup` untimed steps; device syncs on both sides."""
+    import torch
+
+    gw = capture_steps(fn, 0, warmup) if warmup > 0 else None
+    gk = capture_steps(fn, warmup, steps)
+    if gw is not None:
+        gw.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gk.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
     """Mean duration of fn(i)'s launches: `iters` calls back to back between
     two HIP events recorded on the stream the kernels are launched on
@@ -242,7 +273,8 @@ def main(argv=None):
         return 0
     p = workloads.make_workload("paged_decode")
     r = Runner(p)
-    secs = time_steps(r.step, args.steps, args.warmup)
+    eager_secs = time_steps(r.step, args.steps, args.warmup)
+    secs = time_graph_steps(r.step, args.steps, args.warmup)
     ms = 1e3 * secs / args.steps
     b = algorithmic_bytes(p)
     k_us = kernel_time_us(r.transform, max(args.steps, 50))
@@ -262,10 +294,15 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "paged_decode: PAGED, 128 rows x 8192 fp32 N(0,1) scores, k=2048, "
-                               "page_size=64, random page tables; step = plan + paged transform",
+                               "page_size=64, random page tables; step = plan + paged transform "
+                               "on its own cold copy of the scores; the timed steps replay from "
+                               "one captured HIP graph",
                    **describe(p), "page_size": p.page_size,
                    "cold_rotation_copies": r.copies},
         "score_GBps_step": b["score"] * args.steps / secs / 1e9,
+        "eager": {"ms_per_step": 1e3 * eager_secs / args.steps,
+                  "rows_per_s": p.num_rows * args.steps / eager_secs,
+                  "note": "same steps issued call by call from Python (host-bound)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "kernel": "dsatopk::rows_short_kernel<true>", "kernel_us": k_us,

@@ -180,3 +180,51 @@ def test_zero_rows_noop():
     out = dt.ragged(s, lens, lens, 4)
     torch.cuda.synchronize()
     assert out.shape == (0, 4)
+
+
+@pytest.mark.parametrize("name", ["paged_decode", "paged_long", "ragged_extend"])
+def test_graph_replay_matches_eager(orc, name):
+    """plan + transform captured in a HIP graph: every replay, with eager
+    work and synchronizations between replays, selects what the eager call
+    and the oracle select (split rows included: their exchange areas must be
+    zero again for the next replay). Register-path rows are byte-equal; the
+    split path orders a row's outputs by segment arrival."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload(name)
+    print(f"[gpu] graph replay {name}", flush=True)
+    d = gpu_run.to_dev(p)
+    out = torch.empty((p.num_rows, p.k), dtype=torch.int32, device="cuda")
+    plan = dt.plan(d["lens"], p.k, row_starts=d["starts"])
+
+    def step():
+        dt.plan(d["lens"], p.k, row_starts=d["starts"], out=plan)
+        if p.mode == "ragged":
+            dt.ragged(d["scores"], d["lens"], d["offs"], p.k, row_starts=d["starts"], plan=plan,
+                      out=out)
+        else:
+            dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, row_starts=d["starts"],
+                     plan=plan, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    assert_rows_equal(canonical(eager, p.seq_lens, p.k), expected(orc, p), name)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for it in range(4):
+        out.fill_(-5)
+        scratch.add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        if name == "paged_decode":
+            assert np.array_equal(got, eager), f"replay {it} differs from the eager call"
+        assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p),
+                          f"{name} replay {it}")
+    assert _plan_words(plan)[14] == 0, "a segment timed out waiting for its row"
