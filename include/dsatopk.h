@@ -88,21 +88,22 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  * row_starts may be NULL, meaning every window starts at column 0) and
  * writes the plan buffer (device, plan_bytes >= dsatopk_plan_bytes(num_rows),
  * 16-byte aligned): each row's length class (trivial or up to 8192 aligned
- * floats, up to 16384, longer) and the list of rows of each class, so that
- * each class's kernel runs on packed workgroups; and, for up to 512 rows
- * longer than 16384, a cut into segments of 8192 floats served by one
- * workgroup each, with a zeroed exchange area per row through which the
- * segments merge their histograms. Everything is computed on the device;
- * nothing is read back.
+ * floats, up to 16384, longer) with the rows of each class listed, and, for
+ * up to 512 rows longer than 16384, a cut into segments of 8192 floats
+ * served by one workgroup each, with a zeroed exchange area per row through
+ * which the segments merge their histograms. Everything is computed on the
+ * device; nothing is read back. The transform calls read only the split
+ * schedule: rows of the other classes go to their kernel by their own
+ * length, with no plan lookup before their data.
  *
  * The plan only schedules: a call given a plan built from different
  * seq_lens / row_starts / k, or no plan at all (NULL), returns the same
  * outputs (every kernel recomputes each row's class and segment count, and
- * a row that no longer matches its plan is served by the streaming
- * long-row kernel). A plan must come from a dsatopk_plan call with the same
- * num_rows. A plan may be reused by any number of later transform calls
- * (one per layer, say): each call leaves the exchange areas zeroed again.
- * Calls that share one plan must not run concurrently.
+ * a long row that does not match its planned segments is served by the
+ * streaming long-row kernel). A plan must come from a dsatopk_plan call
+ * with the same num_rows. A plan may be reused by any number of later
+ * transform calls (one per layer, say): each call leaves the exchange areas
+ * zeroed again. Calls that share one plan must not run concurrently.
  *
  * Source: PR #26788 digest, "Key source excerpts", plan_topk_v2 (a device
  * plan built from seq_lens and reused by the transform); the layout here is

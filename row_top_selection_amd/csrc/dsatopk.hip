@@ -192,12 +192,18 @@ struct Emit {
 constexpr int kWideBlock = 1024;  // threads per row when rows are too few to fill the chip
 static_assert(kMaxK + kBlock <= kBins, "a split segment's output stage and its dummies fit the histogram");
 
-struct SmemReg {
-  uint32_t hist[kBins];                // every histogram of the row's digits; finally the output stage
-  int32_t pt[kPtCap];                  // the row's page-table entries (PAGED)
-  uint32_t wave_cnt[kWideBlock / 64];  // per wave: selected elements
-  uint32_t bcast[4];                   // a bin search's result, when one wave searches
+template <int BS>
+struct SmemRegB {
+  uint32_t hist[kBins];        // every histogram of the row's digits; finally the output stage
+  int32_t pt[kPtCap];          // the row's page-table entries (PAGED)
+  uint32_t wave_cnt[BS / 64];  // per wave: selected elements
+  uint32_t bcast[4];           // a bin search's result, when one wave searches
+  // per-lane and per-wave running sums of a search shared by all waves
+  // (1024-thread workgroups only)
+  uint32_t lsum[BS > kBlock ? BS : 1];
+  uint32_t wsum[BS / 64];
 };
+using SmemReg = SmemRegB<kBlock>;
 
 // The split path also keeps small digit histograms beside its candidate
 // list, which fills the 4096-word array.
@@ -299,9 +305,21 @@ struct StreamSrc {
   }
 };
 
-template <bool kPaged>
+template <bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L, int32_t k) {
-  for (int32_t t = tix(); t < k; t += kBlock) em.out[t] = t < L ? em.value(t) : -1;
+  // all table loads before any store: one memory round trip, not one per slot
+  constexpr int kIter = kMaxK / BS;
+  int32_t v[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int32_t t = i * BS + tix();
+    v[i] = t < L ? em.value(t) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int32_t t = i * BS + tix();
+    if (t < k) em.out[t] = v[i];
+  }
 }
 
 // Final coalesced store of the k staged positions. A position outside
@@ -341,8 +359,8 @@ __device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_
 // result goes through LDS (one barrier). Several workgroups share a CU, so
 // the issue slots of the idle waves are not lost, while a search by every
 // wave would multiply its VALU work by the wave count.
-template <int NB, bool kDesc, int BS>
-__device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, SmemReg& sm) {
+template <int NB, bool kDesc, class Sm>
+__device__ __forceinline__ BinHit wave0_find(const uint32_t* hist, uint32_t need, Sm& sm) {
   if (wave_id() == 0) {
     const BinHit h = wave_find<NB, kDesc>(hist, need);
     if (lane_id() == 0) {
@@ -357,14 +375,75 @@ __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need
                 (uint32_t)__builtin_amdgcn_readfirstlane(sm.bcast[2])};
 }
 
+// The same search by all W = BS / 64 waves of a workgroup that runs alone
+// on its CU (a latency-bound launch): lane u = 64 w + l sums the run of
+// PER = NB / BS bins at scan positions [u PER, (u + 1) PER); the per-lane
+// running sums of each wave and the wave totals go through LDS; after one
+// barrier every wave finds the crossing wave, then lane, then bin by
+// itself. Its second-level reads of the histogram need a closing barrier
+// before anyone may write it again.
+template <int NB, bool kDesc, int BS>
+__device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t need,
+                                                 SmemRegB<BS>& sm) {
+  constexpr int W = BS / 64;
+  constexpr int PER = NB / BS;
+  static_assert(PER >= 4 && PER % 4 == 0 && PER <= 64 && W <= 64, "one 16-byte read per run step");
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int u = w * 64 + lane;
+  auto bin_of = [](int r) { return kDesc ? NB - 1 - r : r; };  // scan position -> bin
+  uint32_t sum = 0;
+  {
+    const int lo = kDesc ? NB - (u + 1) * PER : u * PER;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist + lo);
+#pragma unroll
+    for (int i = 0; i < PER / 4; ++i) {
+      const uint4 q = h4[i];
+      sum += q.x + q.y + q.z + q.w;
+    }
+  }
+  const uint32_t incl = wave_inclusive_sum(sum);
+  sm.lsum[u] = incl;
+  if (lane == 63) sm.wsum[w] = incl;
+  __syncthreads();
+  const uint32_t tw = lane < W ? sm.wsum[lane] : 0u;
+  const uint32_t iw = wave_inclusive_sum(tw);
+  const uint64_t mw = __ballot(iw >= need);
+  const int wc = mw ? __builtin_ctzll(mw) : W - 1;
+  const uint32_t basew = read_lane(iw - tw, wc);
+  const uint32_t il = basew + sm.lsum[wc * 64 + lane];
+  const uint64_t ml = __ballot(il >= need);
+  const int l1 = ml ? __builtin_ctzll(ml) : 63;
+  const uint32_t before1 = l1 ? read_lane(il, l1 - 1) : basew;
+  const int r0 = (wc * 64 + l1) * PER;
+  const uint32_t v = lane < PER ? hist[bin_of(r0 + lane)] : 0u;
+  const uint32_t incl2 = before1 + wave_inclusive_sum(v);
+  const uint64_t m2 = __ballot((lane < PER) & (incl2 >= need));
+  const int l2 = m2 ? __builtin_ctzll(m2) : 0;
+  BinHit h;
+  h.bin = (uint32_t)bin_of(r0 + l2);
+  h.cnt = read_lane(v, l2);
+  h.before = read_lane(incl2, l2) - h.cnt;
+  __syncthreads();
+  return h;
+}
+
+template <int NB, bool kDesc, int BS, class Sm>
+__device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, Sm& sm) {
+  if constexpr (BS > kBlock && NB >= 4 * BS)
+    return all_waves_find<NB, kDesc, BS>(hist, need, sm);
+  else
+    return wave0_find<NB, kDesc>(hist, need, sm);
+}
+
 // The cut of a register-resident row. Level 1 (key bits 31..20) was
 // histogrammed into sm.hist by the caller. Level 2 takes the next 12 bits
 // (19..8) in the same array, cleared once its level-1 search is done;
 // level 3 the last 8 bits. Each level costs one filtered pass over the
 // registers and a search by wave 0. Ties at the k-th key take two position
 // digits (rare).
-template <int BS, class Src>
-__device__ __forceinline__ Cut refine_in_registers(const Src& src, SmemReg& sm, uint32_t k) {
+template <int BS, class Src, class Sm>
+__device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint32_t k) {
   BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
   uint32_t need = k - h.before;
   uint32_t prefix = h.bin;  // key bits 31..20
@@ -472,103 +551,6 @@ __device__ __forceinline__ void load_row(const RowView& rv, float4 (&x)[NV]) {
   load_vectors<NV, BS>(rv.base4, (rv.span + 3) >> 2, 0, x);
 }
 
-// Positions of the elements `sel` takes, into stage[0 ..) in register
-// order: each thread counts its own, a scan over the workgroup gives its
-// first slot, and a second pass writes them. Without kGuard the caller
-// guarantees that at most k elements are taken.
-template <int BS, bool kGuard, class Src, class Sel>
-__device__ __forceinline__ void stage_selected(const Src& src, Sel sel, uint32_t k,
-                                               int32_t* stage, SmemReg& sm) {
-  const int lane = lane_id();
-  const int w = wave_id();
-  uint32_t mine = 0;
-  src.for_each([&](uint32_t kk, int32_t j) { mine = add_lane_bit(mine, __ballot(sel(kk, j))); });
-  const uint32_t incl = wave_inclusive_sum(mine);
-  if (lane == 63) sm.wave_cnt[w] = incl;
-  __syncthreads();
-  uint32_t slot = incl - mine;
-  for (int v = 0; v < w; ++v) slot += sm.wave_cnt[v];
-  src.for_each([&](uint32_t kk, int32_t j) {
-    const bool s = sel(kk, j);
-    const uint64_t m = __ballot(s);
-    if (kGuard ? (s & (slot < k)) : s) stage[slot] = j;
-    slot = add_lane_bit(slot, m);
-  });
-}
-
-// The rest of the register path, once the row's vectors are in x (and the
-// caller has staged the page table, if it stages it).
-template <int NV, bool kPaged, int BS>
-__device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4 (&x)[NV],
-                                                 int32_t k, Emit<kPaged> em, SmemReg& sm) {
-  const int32_t t = tix();
-  const int32_t L = rv.span - rv.rem;
-  // Register slices 0 .. ilast hold the span's vectors; later slices hold
-  // nothing of the row, and every pass skips them.
-  const int32_t ilast = __builtin_amdgcn_readfirstlane((((rv.span + 3) >> 2) - 1) / BS);
-  uint32_t key[NV][4];
-  clear_bins<kBins, BS>(sm.hist);
-  __syncthreads();
-  // Slice by slice as its loads land: keys, then the level-1 histogram.
-  // Columns outside the window get key 0, below every float's key except
-  // the all-ones NaN: in the first vector the columns before the window
-  // start, and in slice ilast every column at or past the span. All other
-  // columns of slices 0 .. ilast lie inside the window. The outside columns
-  // count in bin 0 like in every later pass, so the counts of all passes
-  // agree.
-  {
-    const uint32_t one = opaque_one();
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (i <= ilast) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
-        if (i == 0 && t == 0) {
-          if (rv.rem > 0) key[0][0] = 0u;
-          if (rv.rem > 1) key[0][1] = 0u;
-          if (rv.rem > 2) key[0][2] = 0u;
-        }
-        if (i == ilast) {
-          const int32_t a = 4 * (i * BS + t);
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (a + c >= rv.span) key[i][c] = 0u;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
-      }
-    }
-  }
-  __syncthreads();
-  const RegSrc<NV, BS> src{key, -rv.rem, ilast};
-  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
-
-  // Stage the selected positions in LDS (the histogram's space, free now),
-  // then one coalesced pass maps and stores the k outputs. Without a
-  // partial tie class (the usual case) the selection is key >= thr, and the
-  // cut's counts make that at most k elements. With one (several elements
-  // hold exactly the k-th key tau and only those at positions <= pos are
-  // taken) the rare second form applies, with a guard on the slot.
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  if (cut.pos == kAllPos) {
-    const uint32_t lo = cut.prefix << cut.shift;
-    const uint32_t thr = lo ? lo : 1u;
-    stage_selected<BS, false>(
-        src, [thr](uint32_t kk, int32_t) { return kk >= thr; }, (uint32_t)k, stage, sm);
-  } else {
-    const uint32_t tau = cut.prefix;
-    const int32_t pos = cut.pos;
-    stage_selected<BS, true>(
-        src,
-        [tau, pos](uint32_t kk, int32_t j) {
-          return (kk != 0u) & ((kk > tau) | ((kk == tau) & (j <= pos)));
-        },
-        (uint32_t)k, stage, sm);
-  }
-  __syncthreads();
-  write_stage<kPaged, BS>(em, stage, L, k, sm.pt);
-}
-
 // The page-table entries of window [0, L) into registers (entry e in
 // v[e / BS] of thread e % BS) when they fit the LDS table, then into the
 // table. The loads are issued before the row's score loads, so the wait for
@@ -610,16 +592,126 @@ __device__ __forceinline__ void store_table(Emit<kPaged>& em, int32_t* lds, int3
   }
 }
 
+// Positions of the elements `sel` takes, into stage[0 ..) in register
+// order: each thread counts its own, a scan over the workgroup gives its
+// first slot, and a second pass writes them. Without kGuard the caller
+// guarantees that at most k elements are taken.
+template <int BS, bool kGuard, class Src, class Sel, class Sm>
+__device__ __forceinline__ void stage_selected(const Src& src, Sel sel, uint32_t k,
+                                               int32_t* stage, Sm& sm) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  uint32_t mine = 0;
+  src.for_each([&](uint32_t kk, int32_t j) { mine = add_lane_bit(mine, __ballot(sel(kk, j))); });
+  const uint32_t incl = wave_inclusive_sum(mine);
+  if (lane == 63) sm.wave_cnt[w] = incl;
+  __syncthreads();
+  uint32_t slot = incl - mine;
+  if constexpr (BS > kBlock) {
+    // the counts of the waves before this one: one read per lane and a scan
+    const uint32_t c = lane < BS / 64 ? sm.wave_cnt[lane] : 0u;
+    const uint32_t ic = wave_inclusive_sum(c);
+    slot += w ? read_lane(ic, w - 1) : 0u;
+  } else {
+    for (int v = 0; v < w; ++v) slot += sm.wave_cnt[v];
+  }
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = sel(kk, j);
+    const uint64_t m = __ballot(s);
+    if (kGuard ? (s & (slot < k)) : s) stage[slot] = j;
+    slot = add_lane_bit(slot, m);
+  });
+}
+
+// The rest of the register path, once the row's vectors are in x (and the
+// caller has staged the page table, if it stages it).
+template <int NV, bool kPaged, int BS>
+__device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4 (&x)[NV],
+                                                 const int32_t (&tv)[table_per_thread<BS>()],
+                                                 int32_t k, Emit<kPaged> em,
+                                                 SmemRegB<BS>& sm) {
+  const int32_t t = tix();
+  const int32_t L = rv.span - rv.rem;
+  // Register slices 0 .. ilast hold the span's vectors; later slices hold
+  // nothing of the row, and every pass skips them.
+  const int32_t ilast = __builtin_amdgcn_readfirstlane((((rv.span + 3) >> 2) - 1) / BS);
+  uint32_t key[NV][4];
+  if constexpr (BS <= kBlock) store_table<kPaged, BS>(em, sm.pt, L, tv);
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
+  // Slice by slice as its loads land: keys, then the level-1 histogram.
+  // Columns outside the window get key 0, below every float's key except
+  // the all-ones NaN: in the first vector the columns before the window
+  // start, and in slice ilast every column at or past the span. All other
+  // columns of slices 0 .. ilast lie inside the window. The outside columns
+  // count in bin 0 like in every later pass, so the counts of all passes
+  // agree.
+  {
+    const uint32_t one = opaque_one();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i <= ilast) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
+        if (i == 0 && t == 0) {
+          if (rv.rem > 0) key[0][0] = 0u;
+          if (rv.rem > 1) key[0][1] = 0u;
+          if (rv.rem > 2) key[0][2] = 0u;
+        }
+        if (i == ilast) {
+          const int32_t a = 4 * (i * BS + t);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (a + c >= rv.span) key[i][c] = 0u;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
+      }
+    }
+  }
+  // A 1024-thread workgroup runs alone on its CU and waits for everything:
+  // it stores the table now, when its loads (issued before the scores) are
+  // in, instead of stalling on them before the clear. Workgroups sharing a
+  // CU hide that stall and keep the registers instead.
+  if constexpr (BS > kBlock) store_table<kPaged, BS>(em, sm.pt, L, tv);
+  __syncthreads();
+  const RegSrc<NV, BS> src{key, -rv.rem, ilast};
+  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
+
+  // Stage the selected positions in LDS (the histogram's space, free now),
+  // then one coalesced pass maps and stores the k outputs. Without a
+  // partial tie class (the usual case) the selection is key >= thr, and the
+  // cut's counts make that at most k elements. With one (several elements
+  // hold exactly the k-th key tau and only those at positions <= pos are
+  // taken) the rare second form applies, with a guard on the slot.
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  if (cut.pos == kAllPos) {
+    const uint32_t lo = cut.prefix << cut.shift;
+    const uint32_t thr = lo ? lo : 1u;
+    stage_selected<BS, false>(
+        src, [thr](uint32_t kk, int32_t) { return kk >= thr; }, (uint32_t)k, stage, sm);
+  } else {
+    const uint32_t tau = cut.prefix;
+    const int32_t pos = cut.pos;
+    stage_selected<BS, true>(
+        src,
+        [tau, pos](uint32_t kk, int32_t j) {
+          return (kk != 0u) & ((kk > tau) | ((kk == tau) & (j <= pos)));
+        },
+        (uint32_t)k, stage, sm);
+  }
+  __syncthreads();
+  write_stage<kPaged, BS>(em, stage, L, k, sm.pt);
+}
+
 template <int NV, bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
-                                                 SmemReg& sm) {
-  const int32_t L = rv.span - rv.rem;
+                                                 SmemRegB<BS>& sm) {
   int32_t tv[table_per_thread<BS>()];
-  load_table<kPaged, BS>(em, L, tv);
+  load_table<kPaged, BS>(em, rv.span - rv.rem, tv);
   float4 x[NV];
   load_row<NV, BS>(rv, x);
-  store_table<kPaged, BS>(em, sm.pt, L, tv);
-  row_from_vectors<NV, kPaged, BS>(rv, x, k, em, sm);
+  row_from_vectors<NV, kPaged, BS>(rv, x, tv, k, em, sm);
 }
 
 // Span too long for registers: stream it. Pass 1 builds the level-1
@@ -724,35 +816,24 @@ __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const Ro
   return rv;
 }
 
-// The row this workgroup serves in a launch for class kClass, or -1.
-// With a plan, workgroup i takes the i-th planned row of the class; a row
-// whose class changed since planning is skipped here and served by the
-// long-row launch instead. Without a plan, workgroup i looks at row i.
-// A plan is used only if it was built for this many rows; every kernel of a
-// call takes the same decision, so each row is served exactly once.
+// Whether a plan was built for this many rows (only the split kernel and
+// the long-row kernel read it: the split rows' schedule and exchange
+// areas).
 __device__ __forceinline__ bool plan_ok(const Params& p) {
   return p.plan && p.plan[kPlanWordMagic] == kPlanMagic && p.plan[kPlanWordRows] == p.num_rows;
 }
 
-template <int kClass>
-__device__ __forceinline__ int64_t class_row_at(const Params& p, bool planned, int32_t i,
-                                                RowInfo& r) {
-  int64_t b = i;
-  if (planned) {
-    const uint32_t li = (uint32_t)p.plan[kPlanWordOffset + kClass] + (uint32_t)i;
-    if (i >= p.plan[kPlanWordCount + kClass] || li >= (uint32_t)p.num_rows) return -1;
-    b = p.plan[kPlanHeaderWords + li];
-    if ((uint64_t)b >= (uint64_t)p.num_rows) return -1;
-  } else if (i >= p.num_rows) {
-    return -1;
-  }
-  r = row_info(p.seq_lens, p.row_starts, p.k, b);
-  return r.cls == kClass ? b : -1;
-}
-
+// Workgroup b serves row b if the row is of class kClass, else nothing
+// (-1). Every kernel derives a row's class from its length and start, so
+// each row is served by exactly one kernel whatever the plan says; the
+// row's data is the first thing a workgroup loads, with no plan lookup
+// before it.
 template <int kClass>
 __device__ __forceinline__ int64_t class_row(const Params& p, RowInfo& r) {
-  return class_row_at<kClass>(p, plan_ok(p), (int32_t)blockIdx.x, r);
+  (void)p;
+  const int64_t b = blockIdx.x;
+  r = row_info(p.seq_lens, p.row_starts, p.k, b);
+  return r.cls == kClass ? b : -1;
 }
 
 // Trivial rows and spans <= 8192 floats, kept in registers.
@@ -780,11 +861,10 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
   if (b < 0) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
-    for (int32_t t = tix(); t < p.k; t += kWideBlock)
-      em.out[t] = t < r.L ? em.value(t) : -1;
+    write_trivial<kPaged, kWideBlock>(em, r.L, p.k);
     return;
   }
-  __shared__ SmemReg sm;
+  __shared__ SmemRegB<kWideBlock> sm;
   row_in_registers<kSmallVec * kBlock / kWideBlock, kPaged, kWideBlock>(row_view(p, b, r), p.k,
                                                                          em, sm);
 }
@@ -815,9 +895,7 @@ template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
   const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
-  const int32_t* planned = plan_ok(p) ? p.plan + kPlanHeaderWords + p.num_rows : nullptr;
-  const bool stale = planned && planned[b] != r.cls;
-  if (!((r.cls == kClassLong && !split_served(p, b, r)) || stale)) return;
+  if (r.cls != kClassLong || split_served(p, b, r)) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
     write_trivial(em, r.L, p.k);
@@ -1268,13 +1346,42 @@ __global__ __launch_bounds__(kBlock) void rows_split_kernel(const Params p) {
   segment_in_registers<kPaged>(p, b, r, seg, S, x, sm, s_word);
 }
 
-// Plan: classify every row and list the rows of each class. One workgroup.
+// Plan: classify every row and list the rows of each class (workgroup 0).
 constexpr int kPlanBlock = 1024;
+
+// Up to this many rows the plan is one launch: its workgroups after the
+// first zero the exchange areas, each counting the batch's long rows by
+// itself (one row per thread) to learn whether its area is assigned. Larger
+// batches zero them in a second launch that reads the count from the plan.
+constexpr int kFusedClearRows = kPlanBlock;
+
+__device__ __forceinline__ void zero_area(int32_t num_rows, int32_t* plan, int32_t q,
+                                          int32_t block) {
+  int32_t* x = plan + plan_xarea_word(num_rows) + (int64_t)q * kXWords;
+  for (int32_t i = tix(); i < kXWords; i += block) x[i] = 0;
+}
 
 __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_lens,
                                                          const int32_t* row_starts,
                                                          int32_t num_rows, int32_t k,
                                                          int32_t* plan) {
+  if (blockIdx.x > 0) {
+    // area q of the split rows: the first min(long rows, cap) are assigned
+    __shared__ uint32_t n_long;
+    if (tix() == 0) n_long = 0;
+    __syncthreads();
+    const int32_t b = tix();
+    const bool lng =
+        b < num_rows && row_info(seq_lens, row_starts, k, b).cls == kClassLong;
+    const uint64_t m = __ballot(lng);
+    if (lane_id() == 0 && m) atomicAdd(&n_long, (uint32_t)__builtin_popcountll(m));
+    __syncthreads();
+    const int64_t cap = plan_split_cap(num_rows);
+    const int32_t q = (int32_t)blockIdx.x - 1;
+    if ((int64_t)q < ((int64_t)n_long < cap ? (int64_t)n_long : cap))
+      zero_area(num_rows, plan, q, kPlanBlock);
+    return;
+  }
   __shared__ uint32_t count[3];
   __shared__ uint32_t fill[3];
   __shared__ uint32_t n_split;
@@ -1339,8 +1446,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
 __global__ __launch_bounds__(kBlock) void plan_clear_kernel(int32_t num_rows, int32_t* plan) {
   const int32_t q = blockIdx.x;
   if (q >= plan[kPlanWordSplit]) return;
-  int32_t* x = plan + plan_xarea_word(num_rows) + (int64_t)q * kXWords;
-  for (int32_t i = tix(); i < kXWords; i += kBlock) x[i] = 0;
+  zero_area(num_rows, plan, q, kBlock);
 }
 
 }  // namespace dsatopk
@@ -1426,10 +1532,13 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
   if (!seq_lens || !plan) return DSATOPK_ERR_INVALID_ARG;
   if (plan_bytes < dsatopk_plan_bytes(num_rows)) return DSATOPK_ERR_PLAN_TOO_SMALL;
   if ((reinterpret_cast<uintptr_t>(plan) & 15u) != 0) return DSATOPK_ERR_ALIGNMENT;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanBlock), 0, (hipStream_t)stream, seq_lens,
-                     row_starts, num_rows, k, (int32_t*)plan);
-  hipLaunchKernelGGL(plan_clear_kernel, dim3((unsigned)plan_split_cap(num_rows)), dim3(kBlock), 0,
-                     (hipStream_t)stream, num_rows, (int32_t*)plan);
+  const int64_t cap = plan_split_cap(num_rows);
+  const bool fused = num_rows <= kFusedClearRows;
+  hipLaunchKernelGGL(plan_kernel, dim3(fused ? (unsigned)(1 + cap) : 1u), dim3(kPlanBlock), 0,
+                     (hipStream_t)stream, seq_lens, row_starts, num_rows, k, (int32_t*)plan);
+  if (!fused)
+    hipLaunchKernelGGL(plan_clear_kernel, dim3((unsigned)cap), dim3(kBlock), 0,
+                       (hipStream_t)stream, num_rows, (int32_t*)plan);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }
 
