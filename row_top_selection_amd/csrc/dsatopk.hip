@@ -222,6 +222,21 @@ struct SmemStream {
   uint32_t ncand;
 };
 
+// Shared memory of the single-pass streaming path: the candidate list and
+// one digit histogram (which ends as the output stage).
+constexpr int kS1Vec = 2;                        // float4 per thread per chunk
+constexpr int kS1Chunk = kS1Vec * 4 * kBlock;    // 2048 elements per chunk
+constexpr int kS1Depth = 4;                      // chunks in flight per workgroup
+constexpr int kS1Cap = kMaxK + kS1Chunk + 512;   // candidate pairs: k, one chunk, slack
+
+struct SmemS1 {
+  uint2 cand[kS1Cap];
+  uint32_t hist[kBins];
+  uint32_t n;  // candidates in cand
+  uint32_t nstage;
+  uint32_t bcast[4];
+};
+
 // Window of one row, addressed from the 16-byte aligned column at or below
 // row_start: aligned index a holds window position a - rem, and only
 // rem <= a < span are in the window.
@@ -274,6 +289,20 @@ struct WaveCandSrc {
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
     for (uint32_t i = lane_id(); i < n; i += 64) {
+      const uint2 e = cand[i];
+      f(e.x, (int32_t)e.y);
+    }
+  }
+};
+
+// (key, position) pairs in LDS, enumerated to the whole workgroup.
+struct GroupCandSrc {
+  const uint2* cand;
+  uint32_t n;
+
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    for (uint32_t i = tix(); i < n; i += kBlock) {
       const uint2 e = cand[i];
       f(e.x, (int32_t)e.y);
     }
@@ -768,6 +797,157 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
   write_stage(em, sm.stage, L, k, nullptr);
 }
 
+// A long row in one pass over its scores. The workgroup streams the row
+// in chunks of 2048 elements, kS1Depth chunks in flight, and keeps in LDS
+// the (key, position) pairs of every element with key >= T. T starts at 1
+// (every window element; columns outside the window have key 0) and only
+// rises: when the list could not take another chunk, T becomes a key no
+// higher than the k-th largest of the list (its 24-bit prefix), and only
+// the pairs >= T stay. The k-th largest of a subset never exceeds the k-th
+// largest of the row, so every pair the row's top k needs is kept. After
+// the last chunk the exact cut (ties included) is resolved over the list.
+// Returns false, having written nothing, when ties keep the list too full
+// to take another chunk; the caller then runs the two-pass path.
+__device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint32_t& T,
+                                                   uint32_t& n) {
+  const int t = tix();
+  clear_bins<kBins>(sm.hist);
+  __syncthreads();
+  for (uint32_t i = t; i < n; i += kBlock) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
+  __syncthreads();
+  const BinHit h = wave0_find<kBins, true>(sm.hist, k, sm);
+  uint32_t Tn = h.bin << 20;
+  if (h.cnt > 64) {
+    clear_bins<kBins>(sm.hist);
+    __syncthreads();
+    for (uint32_t i = t; i < n; i += kBlock) {
+      const uint32_t key = sm.cand[i].x;
+      if ((key >> 20) == h.bin) lds_inc(&sm.hist[(key >> 8) & 0xfffu]);
+    }
+    __syncthreads();
+    const BinHit h2 = wave0_find<kBins, true>(sm.hist, k - h.before, sm);
+    Tn |= h2.bin << 8;
+  }
+  Tn = Tn > T ? Tn : T;
+  constexpr int kPer = (kS1Cap + kBlock - 1) / kBlock;
+  uint2 mine[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = (uint32_t)(j * kBlock + t);
+    mine[j] = i < n ? sm.cand[i] : make_uint2(0u, 0u);
+  }
+  __syncthreads();
+  if (t == 0) sm.n = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    wave_append_pair(mine[j].x >= Tn, mine[j].x, (int32_t)mine[j].y, sm.cand, &sm.n, kS1Cap);
+  __syncthreads();
+  n = __builtin_amdgcn_readfirstlane(sm.n);
+  T = Tn;
+  return n + (uint32_t)kS1Chunk <= (uint32_t)kS1Cap;
+}
+
+template <bool kPaged>
+__device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const Emit<kPaged>& em,
+                                            SmemS1& sm) {
+  const int t = tix();
+  const int32_t nvec = (rv.span + 3) >> 2;
+  const int32_t nchunk = (nvec + kS1Vec * kBlock - 1) / (kS1Vec * kBlock);
+  const __amdgpu_buffer_rsrc_t rs = row_buffer(rv.base4, nvec);
+  const int32_t off = t * 16;
+  if (t == 0) sm.n = 0;
+  uint32_t T = 1;
+  uint32_t n = 0;
+  float4 buf[kS1Depth][kS1Vec];
+  auto issue = [&](float4 (&b)[kS1Vec], int32_t c) {
+#pragma unroll
+    for (int u = 0; u < kS1Vec; ++u)
+      b[u] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, (c * kS1Vec + u) * kBlock * 16,
+                                                        kStreamingLoad));
+  };
+#pragma unroll
+  for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
+  __syncthreads();
+  for (int32_t c0 = 0; c0 < nchunk; c0 += kS1Depth) {
+#pragma unroll
+    for (int d = 0; d < kS1Depth; ++d) {
+      const int32_t c = c0 + d;
+      if (c < nchunk) {
+        if (n + (uint32_t)kS1Chunk > (uint32_t)kS1Cap && !compact_candidates(sm, (uint32_t)k, T, n))
+          return false;
+        // chunk c: keys, then one append per wave for the chunk's pairs >= T
+        const bool edge = (c == 0) | ((c + 1) * kS1Chunk > rv.span);
+        uint32_t key[kS1Vec][4];
+        uint64_t m[kS1Vec][4];
+        uint32_t total = 0;
+#pragma unroll
+        for (int u = 0; u < kS1Vec; ++u) {
+          const int32_t a0 = ((c * kS1Vec + u) * kBlock + t) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = lane_of(buf[d][u], q);
+            key[u][q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
+            m[u][q] = __ballot(key[u][q] >= T);
+            total += (uint32_t)__builtin_popcountll(m[u][q]);
+          }
+        }
+        if (total) {
+          uint32_t base = 0;
+          if (lane_id() == 0) base = atomicAdd(&sm.n, total);
+          base = read_lane(base, 0);
+#pragma unroll
+          for (int u = 0; u < kS1Vec; ++u) {
+            const int32_t a0 = ((c * kS1Vec + u) * kBlock + t) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint64_t mm = m[u][q];
+              const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                  (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+              if (key[u][q] >= T) sm.cand[base + rank] = make_uint2(key[u][q], (uint32_t)(a0 + q - rv.rem));
+              base += (uint32_t)__builtin_popcountll(mm);
+            }
+          }
+        }
+        __syncthreads();
+        n = __builtin_amdgcn_readfirstlane(sm.n);
+      }
+      if (c + kS1Depth < nchunk) issue(buf[d], c + kS1Depth);
+    }
+  }
+  // the exact cut over the list (fewer than k pairs only if the window
+  // holds keys below every candidate threshold, i.e. all-ones NaNs)
+  const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  if (kk == 0) {
+    for (int32_t i = t; i < k; i += kBlock) stage[i] = -1;
+    __syncthreads();
+    write_stage(em, stage, rv.span - rv.rem, k, nullptr);
+    return true;
+  }
+  clear_bins<kBins>(sm.hist);
+  __syncthreads();
+  for (uint32_t i = t; i < n; i += kBlock) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
+  __syncthreads();
+  const BinHit h = wave0_find<kBins, true>(sm.hist, kk, sm);
+  const GroupCandSrc src{sm.cand, n};
+  const Cut cut = refine_cut<false>(src, sm.hist, h.bin, kk - h.before, h.cnt);
+  if (t == 0) sm.nstage = 0;
+  for (int32_t i = kk + t; i < k; i += kBlock) stage[i] = -1;
+  __syncthreads();
+  for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
+    const uint32_t i = i0 + t;
+    uint2 e = make_uint2(0u, 0u);
+    if (i < n) e = sm.cand[i];
+    wave_append((i < n) & is_selected(cut, e.x, (int32_t)e.y), (int32_t)e.y, stage, &sm.nstage,
+                kk);
+  }
+  __syncthreads();
+  write_stage(em, stage, rv.span - rv.rem, k, nullptr);
+  return true;
+}
+
 template <bool kPaged>
 __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b) {
   Emit<kPaged> em;
@@ -901,8 +1081,15 @@ __global__ __launch_bounds__(kBlock) void rows_long_kernel(const Params p) {
     write_trivial(em, r.L, p.k);
     return;
   }
-  __shared__ SmemStream sm;
-  row_streaming(row_view(p, b, r), p.k, em, sm);
+  __shared__ union {
+    SmemS1 one;
+    SmemStream two;
+  } sm;
+  const RowView rv = row_view(p, b, r);
+  if (!row_stream1(rv, p.k, em, sm.one)) {
+    __syncthreads();
+    row_streaming(rv, p.k, em, sm.two);
+  }
 }
 
 // A published round result: round number in bits 63..56, the payload in
