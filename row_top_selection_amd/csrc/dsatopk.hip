@@ -222,18 +222,22 @@ struct SmemStream {
   uint32_t ncand;
 };
 
+// The long-row kernel: 1024 threads per row.
+constexpr int kLongBlock = 1024;
+
 // Shared memory of the single-pass streaming path: the candidate list and
-// one digit histogram (which ends as the output stage).
-constexpr int kS1Vec = 2;                        // float4 per thread per chunk
-constexpr int kS1Chunk = kS1Vec * 4 * kBlock;    // 2048 elements per chunk
-constexpr int kS1Depth = 4;                      // chunks in flight per workgroup
-constexpr int kS1Cap = kMaxK + kS1Chunk + 512;   // candidate pairs: k, one chunk, slack
+// one digit histogram. A chunk is one float4 per thread (4096 elements),
+// kS1Depth chunks are in flight (64 KiB). Two workgroups fit a CU; after a
+// compaction about 2000 pairs of room stay above k + one chunk, so on rows
+// in random order the list is compacted a handful of times per row.
+constexpr int kS1Chunk = 4 * kLongBlock;
+constexpr int kS1Depth = 4;
+constexpr int kS1Cap = 8176;
 
 struct SmemS1 {
   uint2 cand[kS1Cap];
   uint32_t hist[kBins];
   uint32_t n;  // candidates in cand
-  uint32_t nstage;
   uint32_t bcast[4];
 };
 
@@ -295,42 +299,42 @@ struct WaveCandSrc {
   }
 };
 
-// (key, position) pairs in LDS, enumerated to the whole workgroup.
-struct GroupCandSrc {
-  const uint2* cand;
-  uint32_t n;
-
-  template <class F>
-  __device__ __forceinline__ void for_each(F&& f) const {
-    for (uint32_t i = tix(); i < n; i += kBlock) {
-      const uint2 e = cand[i];
-      f(e.x, (int32_t)e.y);
-    }
-  }
-};
-
 // The row re-read from global memory in chunks of kStreamVec float4 per
 // thread. Every thread calls f the same number of times.
+template <int BS>
 struct StreamSrc {
   RowView rv;
 
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
     const int32_t nvec = (rv.span + 3) >> 2;
-    for (int32_t v0 = 0; v0 < nvec; v0 += kBlock * kStreamVec) {
+    for (int32_t v0 = 0; v0 < nvec; v0 += BS * kStreamVec) {
       float4 x[kStreamVec];
 #pragma unroll
       for (int u = 0; u < kStreamVec; ++u) {
-        const int32_t v = v0 + u * kBlock + tix();
+        const int32_t v = v0 + u * BS + tix();
         x[u] = v < nvec ? rv.base4[v] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < kStreamVec; ++u) {
-        const int32_t a0 = (v0 + u * kBlock + tix()) * 4;
+        const int32_t a0 = (v0 + u * BS + tix()) * 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) f(key_at(lane_of(x[u], c), a0 + c, rv), a0 + c - rv.rem);
       }
     }
+  }
+};
+
+// Candidate (key, position) pairs held in registers, NP per thread.
+template <int NP>
+struct CandRegSrc {
+  const uint32_t (&key)[NP];
+  const int32_t (&pos)[NP];
+
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) f(key[j], pos[j]);
   }
 };
 
@@ -748,12 +752,12 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
 // stage and the threshold bin's elements to LDS, where one wave resolves
 // the cut. A threshold bin larger than the LDS buffer is resolved by
 // re-reading the span once per digit instead.
-template <bool kPaged>
+template <bool kPaged, int BS>
 __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, const Emit<kPaged>& em,
                                               SmemStream& sm) {
-  const StreamSrc src{rv};
+  const StreamSrc<BS> src{rv};
   const int32_t L = rv.span - rv.rem;
-  clear_bins<kBins>(sm.hist);
+  clear_bins<kBins, BS>(sm.hist);
   if (tix() == 0) {
     sm.nstage = 0;
     sm.ncand = 0;
@@ -788,39 +792,41 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
     }
   } else {
     // The whole bin is taken, or it is too large for LDS.
-    const Cut cut = refine_cut<false>(src, sm.hist, t1, need, cnt);
+    const Cut cut = refine_cut<false, StreamSrc<BS>, BS>(src, sm.hist, t1, need, cnt);
     src.for_each([&](uint32_t key, int32_t j) {
       wave_append(is_selected(cut, key, j), j, sm.stage, &sm.nstage, kMaxK);
     });
   }
   __syncthreads();
-  write_stage(em, sm.stage, L, k, nullptr);
+  write_stage<kPaged, BS>(em, sm.stage, L, k, nullptr);
 }
 
 // A long row in one pass over its scores. The workgroup streams the row
-// in chunks of 2048 elements, kS1Depth chunks in flight, and keeps in LDS
-// the (key, position) pairs of every element with key >= T. T starts at 1
-// (every window element; columns outside the window have key 0) and only
-// rises: when the list could not take another chunk, T becomes a key no
-// higher than the k-th largest of the list (its 24-bit prefix), and only
-// the pairs >= T stay. The k-th largest of a subset never exceeds the k-th
-// largest of the row, so every pair the row's top k needs is kept. After
-// the last chunk the exact cut (ties included) is resolved over the list.
-// Returns false, having written nothing, when ties keep the list too full
-// to take another chunk; the caller then runs the two-pass path.
+// in chunks, kS1Depth chunks in flight, and keeps in LDS the (key,
+// position) pairs of every element with key >= T. T starts at 1 (every
+// window element; columns outside the window have key 0) and only rises:
+// when the list could not take another chunk, T becomes a key no higher
+// than the k-th largest of the list (its 24-bit prefix), and only the pairs
+// >= T stay. The k-th largest of a subset never exceeds the k-th largest of
+// the row, so every pair the row's top k needs is kept. After the last
+// chunk the pairs go to registers and the register path resolves the exact
+// cut (ties included) and emits. Returns false, having written nothing,
+// when ties keep the list too full to take another chunk; the caller then
+// runs the two-pass path.
+template <int BS>
 __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint32_t& T,
                                                    uint32_t& n) {
   const int t = tix();
-  clear_bins<kBins>(sm.hist);
+  clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
-  for (uint32_t i = t; i < n; i += kBlock) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
+  for (uint32_t i = t; i < n; i += BS) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
   __syncthreads();
   const BinHit h = wave0_find<kBins, true>(sm.hist, k, sm);
   uint32_t Tn = h.bin << 20;
   if (h.cnt > 64) {
-    clear_bins<kBins>(sm.hist);
+    clear_bins<kBins, BS>(sm.hist);
     __syncthreads();
-    for (uint32_t i = t; i < n; i += kBlock) {
+    for (uint32_t i = t; i < n; i += BS) {
       const uint32_t key = sm.cand[i].x;
       if ((key >> 20) == h.bin) lds_inc(&sm.hist[(key >> 8) & 0xfffu]);
     }
@@ -829,122 +835,156 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
     Tn |= h2.bin << 8;
   }
   Tn = Tn > T ? Tn : T;
-  constexpr int kPer = (kS1Cap + kBlock - 1) / kBlock;
+  constexpr int kPer = (kS1Cap + BS - 1) / BS;
   uint2 mine[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const uint32_t i = (uint32_t)(j * kBlock + t);
+    const uint32_t i = (uint32_t)(j * BS + t);
     mine[j] = i < n ? sm.cand[i] : make_uint2(0u, 0u);
   }
   __syncthreads();
   if (t == 0) sm.n = 0;
   __syncthreads();
+  // one LDS atomic per wave for all of its kept pairs
+  uint32_t total = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    wave_append_pair(mine[j].x >= Tn, mine[j].x, (int32_t)mine[j].y, sm.cand, &sm.n, kS1Cap);
+  for (int j = 0; j < kPer; ++j) total += (uint32_t)__builtin_popcountll(__ballot(mine[j].x >= Tn));
+  uint32_t base = 0;
+  if (lane_id() == 0 && total) base = atomicAdd(&sm.n, total);
+  base = read_lane(base, 0);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const bool keep = mine[j].x >= Tn;
+    const uint64_t m = __ballot(keep);
+    const uint32_t rank =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (keep) sm.cand[base + rank] = mine[j];
+    base += (uint32_t)__builtin_popcountll(m);
+  }
   __syncthreads();
   n = __builtin_amdgcn_readfirstlane(sm.n);
   T = Tn;
   return n + (uint32_t)kS1Chunk <= (uint32_t)kS1Cap;
 }
 
-template <bool kPaged>
+template <bool kPaged, int BS>
 __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const Emit<kPaged>& em,
-                                            SmemS1& sm) {
+                                            SmemS1& sm, SmemRegB<BS>& fin) {
+  static_assert(kS1Chunk == 4 * BS, "one float4 per thread per chunk");
   const int t = tix();
   const int32_t nvec = (rv.span + 3) >> 2;
-  const int32_t nchunk = (nvec + kS1Vec * kBlock - 1) / (kS1Vec * kBlock);
+  const int32_t nchunk = (nvec + BS - 1) / BS;
   const __amdgpu_buffer_rsrc_t rs = row_buffer(rv.base4, nvec);
   const int32_t off = t * 16;
   if (t == 0) sm.n = 0;
   uint32_t T = 1;
   uint32_t n = 0;
-  float4 buf[kS1Depth][kS1Vec];
-  auto issue = [&](float4 (&b)[kS1Vec], int32_t c) {
-#pragma unroll
-    for (int u = 0; u < kS1Vec; ++u)
-      b[u] = __builtin_bit_cast(
-          float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, (c * kS1Vec + u) * kBlock * 16,
-                                                        kStreamingLoad));
+  float4 buf[kS1Depth];
+  auto issue = [&](float4& b, int32_t c) {
+    b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, c * BS * 16,
+                                                                         kStreamingLoad));
   };
 #pragma unroll
   for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
   __syncthreads();
-  for (int32_t c0 = 0; c0 < nchunk; c0 += kS1Depth) {
+  // Set when a compaction cannot make room for a chunk (heavy ties): the
+  // chunk loop stops appending and ends at its next turn. No exit from
+  // inside the unrolled body, whose waits for the loads in flight the
+  // compiler counts exactly only on straight-line paths; for the same
+  // reason every buffered chunk is processed and refilled (chunks past the
+  // row are all masked, and loads past the buffer's end return zeros
+  // without touching memory).
+  bool overflow = false;
+  for (int32_t c0 = 0; c0 < nchunk && !overflow; c0 += kS1Depth) {
 #pragma unroll
     for (int d = 0; d < kS1Depth; ++d) {
       const int32_t c = c0 + d;
-      if (c < nchunk) {
-        if (n + (uint32_t)kS1Chunk > (uint32_t)kS1Cap && !compact_candidates(sm, (uint32_t)k, T, n))
-          return false;
-        // chunk c: keys, then one append per wave for the chunk's pairs >= T
-        const bool edge = (c == 0) | ((c + 1) * kS1Chunk > rv.span);
-        uint32_t key[kS1Vec][4];
-        uint64_t m[kS1Vec][4];
-        uint32_t total = 0;
+      if (c < nchunk && !overflow && n + (uint32_t)kS1Chunk > (uint32_t)kS1Cap)
+        overflow = !compact_candidates<BS>(sm, (uint32_t)k, T, n);
+      const uint32_t Tc = overflow ? 0xffffffffu : T;  // no key reaches all ones
+      const bool edge = (c == 0) | ((c + 1) * kS1Chunk > rv.span);
+      const int32_t a0 = (c * BS + t) * 4;
+      uint32_t key[4];
+      uint64_t m[4];
+      uint32_t total = 0;
 #pragma unroll
-        for (int u = 0; u < kS1Vec; ++u) {
-          const int32_t a0 = ((c * kS1Vec + u) * kBlock + t) * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float x = lane_of(buf[d][u], q);
-            key[u][q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
-            m[u][q] = __ballot(key[u][q] >= T);
-            total += (uint32_t)__builtin_popcountll(m[u][q]);
-          }
-        }
-        if (total) {
-          uint32_t base = 0;
-          if (lane_id() == 0) base = atomicAdd(&sm.n, total);
-          base = read_lane(base, 0);
-#pragma unroll
-          for (int u = 0; u < kS1Vec; ++u) {
-            const int32_t a0 = ((c * kS1Vec + u) * kBlock + t) * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint64_t mm = m[u][q];
-              const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                  (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
-              if (key[u][q] >= T) sm.cand[base + rank] = make_uint2(key[u][q], (uint32_t)(a0 + q - rv.rem));
-              base += (uint32_t)__builtin_popcountll(mm);
-            }
-          }
-        }
-        __syncthreads();
-        n = __builtin_amdgcn_readfirstlane(sm.n);
+      for (int q = 0; q < 4; ++q) {
+        const float x = lane_of(buf[d], q);
+        key[q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
+        m[q] = __ballot(key[q] >= Tc);
+        total += (uint32_t)__builtin_popcountll(m[q]);
       }
-      if (c + kS1Depth < nchunk) issue(buf[d], c + kS1Depth);
+      // one LDS atomic per wave for the chunk's pairs
+      if (total) {
+        uint32_t base = 0;
+        if (lane_id() == 0) base = atomicAdd(&sm.n, total);
+        base = read_lane(base, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m[q] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[q], 0u));
+          if (key[q] >= Tc) sm.cand[base + rank] = make_uint2(key[q], (uint32_t)(a0 + q - rv.rem));
+          base += (uint32_t)__builtin_popcountll(m[q]);
+        }
+      }
+      __syncthreads();
+      n = __builtin_amdgcn_readfirstlane(sm.n);
+      issue(buf[d], c + kS1Depth);
     }
   }
-  // the exact cut over the list (fewer than k pairs only if the window
-  // holds keys below every candidate threshold, i.e. all-ones NaNs)
+  if (overflow) return false;
+
+  // The list to registers (key 0 pads: below every threshold, counted in
+  // bin 0 by every pass alike), then the register path's cut and emit.
+  constexpr int kPer = (kS1Cap + BS - 1) / BS;
+  uint32_t ck[kPer];
+  int32_t cp[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t i = (uint32_t)(j * BS + t);
+    const uint2 e = i < n ? sm.cand[i] : make_uint2(0u, 0xffffffffu);
+    ck[j] = e.x;
+    cp[j] = (int32_t)e.y;
+  }
+  __syncthreads();  // fin aliases the list
+  // fewer than k pairs only if the window holds keys below every
+  // threshold, i.e. all-ones NaNs
   const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  int32_t* stage = reinterpret_cast<int32_t*>(fin.hist);
   if (kk == 0) {
-    for (int32_t i = t; i < k; i += kBlock) stage[i] = -1;
+    for (int32_t i = t; i < k; i += BS) stage[i] = -1;
     __syncthreads();
-    write_stage(em, stage, rv.span - rv.rem, k, nullptr);
+    write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
   }
-  clear_bins<kBins>(sm.hist);
+  clear_bins<kBins, BS>(fin.hist);
   __syncthreads();
-  for (uint32_t i = t; i < n; i += kBlock) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
-  __syncthreads();
-  const BinHit h = wave0_find<kBins, true>(sm.hist, kk, sm);
-  const GroupCandSrc src{sm.cand, n};
-  const Cut cut = refine_cut<false>(src, sm.hist, h.bin, kk - h.before, h.cnt);
-  if (t == 0) sm.nstage = 0;
-  for (int32_t i = kk + t; i < k; i += kBlock) stage[i] = -1;
-  __syncthreads();
-  for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
-    const uint32_t i = i0 + t;
-    uint2 e = make_uint2(0u, 0u);
-    if (i < n) e = sm.cand[i];
-    wave_append((i < n) & is_selected(cut, e.x, (int32_t)e.y), (int32_t)e.y, stage, &sm.nstage,
-                kk);
+  {
+    const uint32_t one = opaque_one();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lds_add(&fin.hist[ck[j] >> 20], one);
   }
   __syncthreads();
-  write_stage(em, stage, rv.span - rv.rem, k, nullptr);
+  const CandRegSrc<kPer> src{ck, cp};
+  const Cut cut = refine_in_registers<BS>(src, fin, kk);
+  if (cut.pos == kAllPos) {
+    const uint32_t lo = cut.prefix << cut.shift;
+    const uint32_t thr = lo ? lo : 1u;
+    stage_selected<BS, false>(
+        src, [thr](uint32_t kv, int32_t) { return kv >= thr; }, kk, stage, fin);
+  } else {
+    const uint32_t tau = cut.prefix;
+    const int32_t pos = cut.pos;
+    stage_selected<BS, true>(
+        src,
+        [tau, pos](uint32_t kv, int32_t j) {
+          return (kv != 0u) & ((kv > tau) | ((kv == tau) & (j <= pos)));
+        },
+        kk, stage, fin);
+  }
+  for (int32_t i = (int32_t)kk + t; i < k; i += BS) stage[i] = -1;
+  __syncthreads();
+  write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
   return true;
 }
 
@@ -1068,27 +1108,27 @@ __device__ __forceinline__ bool split_served(const Params& p, int64_t b, const R
   return S >= 2 && S == segments_for(r.span) && slot >= 0 && slot < plan_split_cap(p.num_rows);
 }
 
-// Longer spans, streamed, one workgroup per row: long rows the split kernel
-// does not serve, and any row whose class differs from the plan's (such a
-// row is skipped by the other launches).
+// Longer spans, streamed, one 1024-thread workgroup per row: the long rows
+// the split kernel does not serve.
 template <bool kPaged>
-__global__ __launch_bounds__(kBlock) void rows_long_kernel(const Params p) {
+__global__ __launch_bounds__(kLongBlock) void rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
   const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
   if (r.cls != kClassLong || split_served(p, b, r)) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
-    write_trivial(em, r.L, p.k);
+    write_trivial<kPaged, kLongBlock>(em, r.L, p.k);
     return;
   }
   __shared__ union {
     SmemS1 one;
+    SmemRegB<kLongBlock> fin;
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
-  if (!row_stream1(rv, p.k, em, sm.one)) {
+  if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin)) {
     __syncthreads();
-    row_streaming(rv, p.k, em, sm.two);
+    row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
   }
 }
 
@@ -1682,7 +1722,7 @@ int launch_rows(Params p, hipStream_t stream) {
     const dim3 items((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg));
     hipLaunchKernelGGL((rows_split_kernel<kPaged>), items, block, 0, stream, p);
   }
-  if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, block, 0, stream, p);
+  if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, dim3(kLongBlock), 0, stream, p);
   if (p.num_rows <= kWideRows) {
     hipLaunchKernelGGL((rows_wide_kernel<kPaged>), grid, dim3(kWideBlock), 0, stream, p);
   } else {

@@ -218,7 +218,7 @@ __device__ __forceinline__ bool is_selected(const Cut& c, uint32_t key, int32_t 
 // enumerate every element to that wave. Otherwise executed by the whole
 // workgroup, every wave finding each bin redundantly; it begins and ends
 // with a barrier.
-template <bool kWave, class Src>
+template <bool kWave, class Src, int BS = kBlock>
 __device__ __forceinline__ Cut refine_cut(const Src src, uint32_t* hist, uint32_t prefix,
                                           uint32_t need, uint32_t cnt) {
   if (cnt == need) return Cut{20, prefix, kAllPos};
@@ -226,7 +226,7 @@ __device__ __forceinline__ Cut refine_cut(const Src src, uint32_t* hist, uint32_
     if constexpr (kWave) wave_lds_sync(); else __syncthreads();
   };
   auto clear4096 = [&] {
-    if constexpr (kWave) wave_clear_bins<kBins>(hist); else clear_bins<kBins>(hist);
+    if constexpr (kWave) wave_clear_bins<kBins>(hist); else clear_bins<kBins, BS>(hist);
   };
 
   // level 2: key bits 19..8 inside bin t1
@@ -247,7 +247,7 @@ __device__ __forceinline__ Cut refine_cut(const Src src, uint32_t* hist, uint32_
   if (h.cnt != need) {
     // level 3: key bits 7..0
     sync();
-    if constexpr (kWave) wave_clear_bins<256>(hist); else clear_bins<256>(hist);
+    if constexpr (kWave) wave_clear_bins<256>(hist); else clear_bins<256, BS>(hist);
     sync();
     {
       const uint32_t p = prefix;
@@ -275,7 +275,7 @@ __device__ __forceinline__ Cut refine_cut(const Src src, uint32_t* hist, uint32_
       need -= h.before;
       const uint32_t hi = h.bin;
       sync();
-      if constexpr (kWave) wave_clear_bins<32>(hist); else clear_bins<32>(hist);
+      if constexpr (kWave) wave_clear_bins<32>(hist); else clear_bins<32, BS>(hist);
       sync();
       src.for_each([&](uint32_t key, int32_t j) {
         if ((key == tau) & (((uint32_t)j >> 5) == hi)) lds_inc(&hist[(uint32_t)j & 31u]);
