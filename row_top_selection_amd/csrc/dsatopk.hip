@@ -88,7 +88,11 @@ enum PlanWord : int32_t {
 // CDNA has no clusters or distributed shared memory).
 constexpr int kSegLen = kSmallVec * 4 * kBlock;                                  // 8192
 constexpr int kMaxSeg = (DSATOPK_MAX_SEQ_LEN + 3 + kSegLen - 1) / kSegLen;         // 17
-constexpr int kMaxSplitRows = 512;
+// A batch's long rows are split only if there are at most this many (about
+// one per CU): each then gets the whole GPU's help. With more, the GPU is
+// already full with one streaming workgroup per long row, which does less
+// work per element than the split rows' merge rounds.
+constexpr int kMaxSplitRows = 256;
 constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
 
 // Exchange area of one split row (int32 words). Every region is zero at
@@ -1605,7 +1609,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     __syncthreads();
     const int64_t cap = plan_split_cap(num_rows);
     const int32_t q = (int32_t)blockIdx.x - 1;
-    if ((int64_t)q < ((int64_t)n_long < cap ? (int64_t)n_long : cap))
+    if ((int64_t)n_long <= cap && (int64_t)q < (int64_t)n_long)
       zero_area(num_rows, plan, q, kPlanBlock);
     return;
   }
@@ -1631,18 +1635,21 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     const RowInfo r = row_info(seq_lens, row_starts, k, b);
     cls[b] = r.cls;
     atomicAdd(&count[r.cls], 1u);
+  }
+  __syncthreads();
+  // the long rows are split all (at most cap of them) or none
+  const bool split = count[kClassLong] <= cap;
+  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     int32_t S = 0;
     int32_t q = -1;
-    if (r.cls == kClassLong) {
-      const uint32_t i = atomicAdd(&n_split, 1u);
-      if (i < cap) {
-        S = segments_for(r.span);
-        q = (int32_t)i;
-        const uint32_t at = atomicAdd(&n_items, (uint32_t)S);
-        for (int32_t sg = 0; sg < S; ++sg) {
-          items[2 * (at + sg)] = b;
-          items[2 * (at + sg) + 1] = sg;
-        }
+    if (split && cls[b] == kClassLong) {
+      const RowInfo r = row_info(seq_lens, row_starts, k, b);
+      S = segments_for(r.span);
+      q = (int32_t)atomicAdd(&n_split, 1u);
+      const uint32_t at = atomicAdd(&n_items, (uint32_t)S);
+      for (int32_t sg = 0; sg < S; ++sg) {
+        items[2 * (at + sg)] = b;
+        items[2 * (at + sg) + 1] = sg;
       }
     }
     nseg[b] = S;
@@ -1663,7 +1670,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
       plan[kPlanWordCount + c] = (int32_t)count[c];
       plan[kPlanWordOffset + c] = (int32_t)off[c];
     }
-    plan[kPlanWordSplit] = (int32_t)(n_split < cap ? n_split : cap);
+    plan[kPlanWordSplit] = (int32_t)n_split;
     plan[kPlanWordItems] = (int32_t)n_items;
     plan[kPlanWordError] = 0;
   }

@@ -15,6 +15,10 @@ from workloads.edge import PATTERNS, edge_batch
 
 pytestmark = pytest.mark.gpu
 
+# long rows of a batch are split when there are at most this many (the plan
+# buffer reserves this many exchange areas)
+SPLIT_CAP = 256
+
 
 @pytest.fixture(scope="module")
 def orc(oracle_mod):
@@ -117,7 +121,7 @@ def test_plan_reuse_and_exchange_reset(orc, name):
     assert words[14] == 0, "a segment timed out waiting for its row"
     R = p.num_rows
     items_word = 64 + 4 * R
-    cap = min(R, 512)
+    cap = min(R, SPLIT_CAP)
     xwords = 16704
     xarea = (items_word + 2 * cap * 17 + 63) // 64 * 64
     x = words[xarea: xarea + n_split * xwords].reshape(n_split, xwords)
@@ -228,3 +232,21 @@ def test_graph_replay_matches_eager(orc, name):
         assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p),
                           f"{name} replay {it}")
     assert _plan_words(plan)[14] == 0, "a segment timed out waiting for its row"
+
+
+def test_many_long_rows_are_streamed(orc):
+    """More long rows than the split path takes: the plan splits none of
+    them and every long row is streamed by one workgroup."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.scaled_long(SPLIT_CAP + 1)
+    print(f"[gpu] {p.name} streamed", flush=True)
+    d = gpu_run.to_dev(p)
+    plan = dt.plan(d["lens"], p.k)
+    torch.cuda.synchronize()
+    assert _plan_words(plan)[12] == 0, "no row may be split"
+    got, ok = gpu_run.run(p, d, use_plan=True)
+    assert ok
+    assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
