@@ -10,9 +10,11 @@ serving loop issues them; the same steps issued call by call from Python are
 reported beside it ("eager"), where host launch overhead dominates.
 
 Also reported (same JSON line):
-  roofline      the paged transform kernel: algorithmic bytes per launch
+  roofline      the paged transform kernel (rows_wide_kernel<true>: 128 short
+                rows, 1024 threads per row): algorithmic bytes per launch
                 (scores of rows with L > k, outputs, page-table entries,
-                lengths) over its mean launch time from HIP events.
+                lengths) over its mean launch time from HIP events around a
+                graph of back-to-back launches.
   sustained     the same per-row shapes with enough rows for >= 1 GiB of
                 scores per launch (paged_decode x32768, paged_long x2048).
   workloads     every named workload, one launch per iteration, cold.
@@ -36,7 +38,7 @@ METRIC = "DSA top-k rows/s + achieved HBM GB/s (paged decode, L=8K–128K, k=204
 HBM_PEAK_GBPS = 8000.0
 ROTATION_BYTES = 1 << 30
 COPY_CALIBRATION_BYTES = 256 << 20
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_rows_short_kernel_paged_decode.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_rows_wide_kernel_paged_decode.md")
 
 
 def kernel_source_hash() -> str:
@@ -181,19 +183,21 @@ def time_graph_steps(fn, steps: int, warmup: int) -> float:
 
 
 def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
-    """Mean duration of fn(i)'s launches: `iters` calls back to back between
-    two HIP events recorded on the stream the kernels are launched on
-    (torch's current stream), divided by `iters`."""
+    """Mean duration of fn(i)'s launches: `iters` calls captured back to back
+    in one HIP graph, replayed between two HIP events recorded on the stream
+    the graph runs on (torch's current stream), divided by `iters`. The graph
+    keeps host launch overhead out of short launches."""
     import torch
 
     for i in range(warmup):
         fn(i)
+    g = capture_steps(fn, warmup, iters)
+    g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for i in range(iters):
-        fn(warmup + i)
+    g.replay()
     b.record()
     torch.cuda.synchronize()
     return 1e3 * a.elapsed_time(b) / iters
@@ -305,7 +309,7 @@ def main(argv=None):
                   "note": "same steps issued call by call from Python (host-bound)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "kernel": "dsatopk::rows_short_kernel<true>", "kernel_us": k_us,
+                     "kernel": "dsatopk::rows_wide_kernel<true>", "kernel_us": k_us,
                      "kernel_source_hash": kernel_source_hash(),
                      "bytes_per_launch": b, "score_GBps": b["score"] / (k_us * 1e3),
                      "plan_us": plan_us},
