@@ -820,25 +820,32 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
 template <int BS>
 __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint32_t& T,
                                                    uint32_t& n) {
+  // Digits of the offset above T, not of the key: the list's keys all sit
+  // just above T, so their top bits share a few bins (LDS atomic
+  // contention), while their offsets spread. Bin (key - T) >> 12, the last
+  // bin taking every larger offset; the lowest key of any bin is a valid
+  // new T, the bin holding the k-th largest giving the highest one.
   const int t = tix();
   clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
-  for (uint32_t i = t; i < n; i += BS) lds_inc(&sm.hist[sm.cand[i].x >> 20]);
+  for (uint32_t i = t; i < n; i += BS) {
+    const uint32_t r = (sm.cand[i].x - T) >> 12;
+    lds_inc(&sm.hist[r < (uint32_t)kBins ? r : (uint32_t)kBins - 1u]);
+  }
   __syncthreads();
   const BinHit h = wave0_find<kBins, true>(sm.hist, k, sm);
-  uint32_t Tn = h.bin << 20;
-  if (h.cnt > 64) {
+  uint32_t Tn = T + (h.bin << 12);
+  if (h.cnt > 64 && h.bin < (uint32_t)kBins - 1u) {
     clear_bins<kBins, BS>(sm.hist);
     __syncthreads();
     for (uint32_t i = t; i < n; i += BS) {
-      const uint32_t key = sm.cand[i].x;
-      if ((key >> 20) == h.bin) lds_inc(&sm.hist[(key >> 8) & 0xfffu]);
+      const uint32_t r = sm.cand[i].x - T;
+      if ((r >> 12) == h.bin) lds_inc(&sm.hist[r & 0xfffu]);
     }
     __syncthreads();
     const BinHit h2 = wave0_find<kBins, true>(sm.hist, k - h.before, sm);
-    Tn |= h2.bin << 8;
+    Tn += h2.bin;
   }
-  Tn = Tn > T ? Tn : T;
   constexpr int kPer = (kS1Cap + BS - 1) / BS;
   uint2 mine[kPer];
 #pragma unroll
@@ -888,9 +895,93 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, c * BS * 16,
                                                                          kStreamingLoad));
   };
+  // Pairs (key[q], a0 + q - rem) with sel[q] to the list: one LDS atomic
+  // per wave for the four.
+  auto append4 = [&](const uint32_t (&key)[4], const bool (&sel)[4], int32_t a0) {
+    uint64_t m[4];
+    uint32_t total = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m[q] = __ballot(sel[q]);
+      total += (uint32_t)__builtin_popcountll(m[q]);
+    }
+    if (total) {
+      uint32_t base = 0;
+      if (lane_id() == 0) base = atomicAdd(&sm.n, total);
+      base = read_lane(base, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m[q] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[q], 0u));
+        if (sel[q]) sm.cand[base + rank] = make_uint2(key[q], (uint32_t)(a0 + q - rv.rem));
+        base += (uint32_t)__builtin_popcountll(m[q]);
+      }
+    }
+  };
 #pragma unroll
   for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
-  __syncthreads();
+
+  // Warm start: the first kS1Depth chunks (16384 elements; a long span has
+  // more) are a register row. Their exact cut gives T (the k-th largest key
+  // of a subset, so no higher than the row's) and their k winners open the
+  // list, in place of the compactions a list starting from T = 1 needs to
+  // climb there.
+  {
+    uint32_t wk[kS1Depth][4];
+#pragma unroll
+    for (int d = 0; d < kS1Depth; ++d) {
+      const int32_t a0 = (d * BS + t) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x = lane_of(buf[d], q);
+        wk[d][q] = d == 0 ? key_at(x, a0 + q, rv) : order_key(x);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kS1Depth; ++d) issue(buf[d], kS1Depth + d);
+    clear_bins<kBins, BS>(fin.hist);
+    __syncthreads();
+    {
+      const uint32_t one = opaque_one();
+#pragma unroll
+      for (int d = 0; d < kS1Depth; ++d)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lds_add(&fin.hist[wk[d][q] >> 20], one);
+    }
+    __syncthreads();
+    const RegSrc<kS1Depth, BS> src{wk, -rv.rem, kS1Depth - 1};
+    const Cut cut = refine_in_registers<BS>(src, fin, (uint32_t)k);
+    __syncthreads();  // fin aliases the list
+    if (t == 0) sm.n = 0;
+    __syncthreads();
+    uint32_t tau;
+    if (cut.pos == kAllPos) {
+      const uint32_t lo = cut.prefix << cut.shift;
+      tau = lo ? lo : 1u;
+#pragma unroll
+      for (int d = 0; d < kS1Depth; ++d) {
+        const bool sel[4] = {wk[d][0] >= tau, wk[d][1] >= tau, wk[d][2] >= tau, wk[d][3] >= tau};
+        append4(wk[d], sel, (d * BS + t) * 4);
+      }
+    } else {
+      tau = cut.prefix;
+      const int32_t pos = cut.pos;
+#pragma unroll
+      for (int d = 0; d < kS1Depth; ++d) {
+        const int32_t a0 = (d * BS + t) * 4;
+        bool sel[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t kv = wk[d][q];
+          sel[q] = (kv != 0u) & ((kv > tau) | ((kv == tau) & (a0 + q - rv.rem <= pos)));
+        }
+        append4(wk[d], sel, a0);
+      }
+    }
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(sm.n);
+    T = tau > 1u ? tau : 1u;
+  }
   // Set when a compaction cannot make room for a chunk (heavy ties): the
   // chunk loop stops appending and ends at its next turn. No exit from
   // inside the unrolled body, whose waits for the loads in flight the
@@ -899,38 +990,24 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // row are all masked, and loads past the buffer's end return zeros
   // without touching memory).
   bool overflow = false;
-  for (int32_t c0 = 0; c0 < nchunk && !overflow; c0 += kS1Depth) {
+  for (int32_t c0 = kS1Depth; c0 < nchunk && !overflow; c0 += kS1Depth) {
 #pragma unroll
     for (int d = 0; d < kS1Depth; ++d) {
       const int32_t c = c0 + d;
       if (c < nchunk && !overflow && n + (uint32_t)kS1Chunk > (uint32_t)kS1Cap)
         overflow = !compact_candidates<BS>(sm, (uint32_t)k, T, n);
       const uint32_t Tc = overflow ? 0xffffffffu : T;  // no key reaches all ones
-      const bool edge = (c == 0) | ((c + 1) * kS1Chunk > rv.span);
+      const bool edge = (c + 1) * kS1Chunk > rv.span;
       const int32_t a0 = (c * BS + t) * 4;
       uint32_t key[4];
-      uint64_t m[4];
-      uint32_t total = 0;
+      bool sel[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float x = lane_of(buf[d], q);
         key[q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
-        m[q] = __ballot(key[q] >= Tc);
-        total += (uint32_t)__builtin_popcountll(m[q]);
+        sel[q] = key[q] >= Tc;
       }
-      // one LDS atomic per wave for the chunk's pairs
-      if (total) {
-        uint32_t base = 0;
-        if (lane_id() == 0) base = atomicAdd(&sm.n, total);
-        base = read_lane(base, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(m[q] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[q], 0u));
-          if (key[q] >= Tc) sm.cand[base + rank] = make_uint2(key[q], (uint32_t)(a0 + q - rv.rem));
-          base += (uint32_t)__builtin_popcountll(m[q]);
-        }
-      }
+      append4(key, sel, a0);
       __syncthreads();
       n = __builtin_amdgcn_readfirstlane(sm.n);
       issue(buf[d], c + kS1Depth);
@@ -960,6 +1037,28 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     __syncthreads();
     write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
+  }
+  // Offsets above T spread where the keys bunch (see the compaction): when
+  // fewer than kk pairs sit 2^24 - 2 or more above T, the cut runs on
+  // (min(key - T, 2^24 - 2) + 1) << 8, exact below that bound and above
+  // the pads' 0, so every saturated pair lies above the cut and is taken.
+  {
+    constexpr uint32_t kSat = (1u << 24) - 2u;
+    uint32_t sat = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      sat += (uint32_t)__builtin_popcountll(__ballot((ck[j] != 0u) & (ck[j] - T >= kSat)));
+    if (t == 0) fin.bcast[3] = 0;
+    __syncthreads();
+    if (lane_id() == 0 && sat) atomicAdd(&fin.bcast[3], sat);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(fin.bcast[3]) < kk) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t r = ck[j] - T;
+        ck[j] = ck[j] ? ((r < kSat ? r : kSat) + 1u) << 8 : 0u;
+      }
+    }
   }
   clear_bins<kBins, BS>(fin.hist);
   __syncthreads();
@@ -1115,7 +1214,8 @@ __device__ __forceinline__ bool split_served(const Params& p, int64_t b, const R
 // Longer spans, streamed, one 1024-thread workgroup per row: the long rows
 // the split kernel does not serve.
 template <bool kPaged>
-__global__ __launch_bounds__(kLongBlock) void rows_long_kernel(const Params p) {
+__global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
+rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
   const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
   if (r.cls != kClassLong || split_served(p, b, r)) return;
