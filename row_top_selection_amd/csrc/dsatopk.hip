@@ -887,7 +887,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   const int32_t nchunk = (nvec + BS - 1) / BS;
   const __amdgpu_buffer_rsrc_t rs = row_buffer(rv.base4, nvec);
   const int32_t off = t * 16;
-  if (t == 0) sm.n = 0;
+  if (t == 0) {
+    sm.n = 0;
+    sm.bcast[3] = 0;  // the final cut's count of saturated offsets
+  }
   uint32_t T = 1;
   uint32_t n = 0;
   float4 buf[kS1Depth];
@@ -916,6 +919,39 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         if (sel[q]) sm.cand[base + rank] = make_uint2(key[q], (uint32_t)(a0 + q - rv.rem));
         base += (uint32_t)__builtin_popcountll(m[q]);
       }
+    }
+  };
+  // The warm-start subset's pairs that `sel` takes, to the list: one LDS
+  // atomic per wave for all of them.
+  auto append_all = [&](const uint32_t (&wk)[kS1Depth][4], auto sel) {
+    const uint64_t below = (1ull << lane_id()) - 1ull;  // lanes under this one
+    constexpr int kHalf = kS1Depth / 2;  // two batches: fewer live lane masks
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint64_t m[kHalf][4];
+      uint32_t total = 0;
+#pragma unroll
+      for (int e = 0; e < kHalf; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d = h * kHalf + e;
+          m[e][q] = __ballot(sel(wk[d][q], (d * BS + t) * 4 + q - rv.rem));
+          total += (uint32_t)__builtin_popcountll(m[e][q]);
+        }
+      uint32_t base = 0;
+      if (lane_id() == 0 && total) base = atomicAdd(&sm.n, total);
+      base = read_lane(base, 0);
+#pragma unroll
+      for (int e = 0; e < kHalf; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d = h * kHalf + e;
+          const uint64_t mm = m[e][q];
+          if ((mm >> lane_id()) & 1ull)
+            sm.cand[base + (uint32_t)__builtin_popcountll(mm & below)] =
+                make_uint2(wk[d][q], (uint32_t)((d * BS + t) * 4 + q - rv.rem));
+          base += (uint32_t)__builtin_popcountll(mm);
+        }
     }
   };
 #pragma unroll
@@ -949,33 +985,35 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         for (int q = 0; q < 4; ++q) lds_add(&fin.hist[wk[d][q] >> 20], one);
     }
     __syncthreads();
-    const RegSrc<kS1Depth, BS> src{wk, -rv.rem, kS1Depth - 1};
-    const Cut cut = refine_in_registers<BS>(src, fin, (uint32_t)k);
-    __syncthreads();  // fin aliases the list
-    if (t == 0) sm.n = 0;
-    __syncthreads();
+    // The level-1 bin of the subset's k-th largest key: its lowest key is a
+    // valid T, and the pairs at or above it (k plus the rest of that bin)
+    // open the list when they fit; else the exact cut of the subset, which
+    // opens it with exactly k.
+    const BinHit h = group_find<kBins, true, BS>(fin.hist, (uint32_t)k, fin);
     uint32_t tau;
-    if (cut.pos == kAllPos) {
-      const uint32_t lo = cut.prefix << cut.shift;
-      tau = lo ? lo : 1u;
-#pragma unroll
-      for (int d = 0; d < kS1Depth; ++d) {
-        const bool sel[4] = {wk[d][0] >= tau, wk[d][1] >= tau, wk[d][2] >= tau, wk[d][3] >= tau};
-        append4(wk[d], sel, (d * BS + t) * 4);
-      }
+    if (h.before + h.cnt <= (uint32_t)(kS1Cap - kS1Chunk)) {
+      __syncthreads();  // fin aliases the list
+      if (t == 0) sm.n = 0;
+      __syncthreads();
+      tau = h.bin << 20;
+      tau = tau ? tau : 1u;
+      append_all(wk, [tau](uint32_t kv, int32_t) { return kv >= tau; });
     } else {
-      tau = cut.prefix;
-      const int32_t pos = cut.pos;
-#pragma unroll
-      for (int d = 0; d < kS1Depth; ++d) {
-        const int32_t a0 = (d * BS + t) * 4;
-        bool sel[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t kv = wk[d][q];
-          sel[q] = (kv != 0u) & ((kv > tau) | ((kv == tau) & (a0 + q - rv.rem <= pos)));
-        }
-        append4(wk[d], sel, a0);
+      const RegSrc<kS1Depth, BS> src{wk, -rv.rem, kS1Depth - 1};
+      const Cut cut = refine_in_registers<BS>(src, fin, (uint32_t)k);
+      __syncthreads();  // fin aliases the list
+      if (t == 0) sm.n = 0;
+      __syncthreads();
+      if (cut.pos == kAllPos) {
+        const uint32_t lo = cut.prefix << cut.shift;
+        tau = lo ? lo : 1u;
+        append_all(wk, [tau](uint32_t kv, int32_t) { return kv >= tau; });
+      } else {
+        tau = cut.prefix;
+        const int32_t pos = cut.pos;
+        append_all(wk, [tau, pos](uint32_t kv, int32_t j) {
+          return (kv != 0u) & ((kv > tau) | ((kv == tau) & (j <= pos)));
+        });
       }
     }
     __syncthreads();
@@ -1027,6 +1065,20 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     ck[j] = e.x;
     cp[j] = (int32_t)e.y;
   }
+  // Offsets above T spread where the keys bunch (see the compaction): when
+  // fewer than the k taken pairs sit 2^24 - 2 or more above T, the cut
+  // runs on (min(key - T, 2^24 - 2) + 1) << 8, exact below that bound and
+  // above the pads' 0, so every saturated pair lies above the cut and is
+  // taken. The count goes through a word the final phase's LDS does not
+  // overlay.
+  constexpr uint32_t kSat = (1u << 24) - 2u;
+  {
+    uint32_t sat = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      sat += (uint32_t)__builtin_popcountll(__ballot((ck[j] != 0u) & (ck[j] - T >= kSat)));
+    if (lane_id() == 0 && sat) atomicAdd(&sm.bcast[3], sat);
+  }
   __syncthreads();  // fin aliases the list
   // fewer than k pairs only if the window holds keys below every
   // threshold, i.e. all-ones NaNs
@@ -1038,26 +1090,11 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
   }
-  // Offsets above T spread where the keys bunch (see the compaction): when
-  // fewer than kk pairs sit 2^24 - 2 or more above T, the cut runs on
-  // (min(key - T, 2^24 - 2) + 1) << 8, exact below that bound and above
-  // the pads' 0, so every saturated pair lies above the cut and is taken.
-  {
-    constexpr uint32_t kSat = (1u << 24) - 2u;
-    uint32_t sat = 0;
+  if (__builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      sat += (uint32_t)__builtin_popcountll(__ballot((ck[j] != 0u) & (ck[j] - T >= kSat)));
-    if (t == 0) fin.bcast[3] = 0;
-    __syncthreads();
-    if (lane_id() == 0 && sat) atomicAdd(&fin.bcast[3], sat);
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(fin.bcast[3]) < kk) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t r = ck[j] - T;
-        ck[j] = ck[j] ? ((r < kSat ? r : kSat) + 1u) << 8 : 0u;
-      }
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t r = ck[j] - T;
+      ck[j] = ck[j] ? ((r < kSat ? r : kSat) + 1u) << 8 : 0u;
     }
   }
   clear_bins<kBins, BS>(fin.hist);
