@@ -1100,9 +1100,13 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   clear_bins<kBins, BS>(fin.hist);
   __syncthreads();
   {
+    // Pads stay out of the count: they sit below every pair (which holds
+    // at least kk), so the search from the top never reaches them, and
+    // thousands of same-bin LDS atomics would serialize.
     const uint32_t one = opaque_one();
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) lds_add(&fin.hist[ck[j] >> 20], one);
+    for (int j = 0; j < kPer; ++j)
+      if (ck[j]) lds_add(&fin.hist[ck[j] >> 20], one);
   }
   __syncthreads();
   const CandRegSrc<kPer> src{ck, cp};
