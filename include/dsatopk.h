@@ -88,8 +88,9 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  * row_starts may be NULL, meaning every window starts at column 0) and
  * writes the plan buffer (device, plan_bytes >= dsatopk_plan_bytes(num_rows),
  * 16-byte aligned): each row's length class (trivial or up to 8192 aligned
- * floats, up to 16384, longer) with the rows of each class listed, and, when
- * the batch has at most 256 rows longer than 16384, a cut of each of them
+ * floats, up to 16384, up to 32768, longer) with the rows of each class
+ * listed, and, when the batch has at most 256 rows longer than 32768, a cut
+ * of each of them
  * into segments of 8192 floats served by one workgroup each, with a zeroed
  * exchange area per row through which the segments merge their histograms
  * (with more long rows, each is streamed by one workgroup). Everything is computed on the

@@ -42,6 +42,8 @@ namespace dsatopk {
 
 constexpr int kSmallVec = 8;          // float4 per thread: 8192-float spans
 constexpr int kLargeVec = 16;         // float4 per thread: 16384-float spans
+constexpr int kBigBlock = 512;        // threads per big register row
+constexpr int kBigVec = 16;           // float4 per thread of those: 32768-float spans
 constexpr int kStreamVec = 8;         // float4 per thread per streaming chunk
 constexpr int kStreamCandCap = 2048;  // streaming path: threshold-bin pairs in LDS
 constexpr int kPtCap = 512;           // page-table entries staged in LDS
@@ -64,7 +66,8 @@ struct Params {
 // Row classes by aligned span. A row's class is recomputed by every kernel
 // from the current seq_lens / row_starts; the plan only packs the rows of a
 // class into the first workgroups of that class's launch.
-enum RowClass : int32_t { kClassShort = 0, kClassMid = 1, kClassLong = 2 };
+enum RowClass : int32_t { kClassShort = 0, kClassMid = 1, kClassBig = 2, kClassLong = 3 };
+constexpr int kNumClasses = 4;
 
 // Plan layout (int32 words): header, then the rows of each class
 // (segments in class order), then each row's class at planning time.
@@ -74,8 +77,8 @@ enum PlanWord : int32_t {
   kPlanWordMagic = 0,
   kPlanWordRows = 1,
   kPlanWordK = 2,
-  kPlanWordCount = 4,   // [3] rows per class
-  kPlanWordOffset = 8,  // [3] first list index per class
+  kPlanWordCount = 4,   // [4] rows per class
+  kPlanWordOffset = 8,  // [4] first list index per class
   kPlanWordSplit = 12,  // long rows cut into segments (each owns an exchange area)
   kPlanWordItems = 13,  // (row, segment) work items of those rows
   kPlanWordError = 14,  // set if a segment ever gave up waiting (never, if correct)
@@ -206,6 +209,7 @@ struct SmemRegB {
   // (1024-thread workgroups only)
   uint32_t lsum[BS > kBlock ? BS : 1];
   uint32_t wsum[BS / 64];
+  uint32_t tie_n;  // slots taken by a small tie class's positions
 };
 using SmemReg = SmemRegB<kBlock>;
 
@@ -473,14 +477,53 @@ __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need
     return wave0_find<NB, kDesc>(hist, need, sm);
 }
 
+// The need-th lowest window position among the elements whose key is tau
+// (not 0: window elements only, so positions are >= 0 and below 2^17),
+// when cnt <= 64 hold it. Their positions go to LDS, one atomic slot each;
+// then every wave picks the need-th lowest by itself, one position bit at
+// a time from the top, on lane masks (positions are distinct). The caller
+// has zeroed sm.tie_n behind at least one barrier, and the histogram is
+// free. The positions are read before the caller's next barrier, so the
+// histogram may be written after it.
+template <class Src, class Sm>
+__device__ __forceinline__ int32_t small_tie_pos(const Src& src, Sm& sm, uint32_t tau,
+                                                 uint32_t cnt, uint32_t need) {
+  uint32_t* tie = sm.hist;
+  src.for_each([&](uint32_t kk, int32_t j) {
+    if (kk == tau) {
+      const uint32_t slot = atomicAdd(&sm.tie_n, 1u);
+      if (slot < 64u) tie[slot] = (uint32_t)j;
+    }
+  });
+  __syncthreads();
+  const int lane = lane_id();
+  const uint32_t p = lane < (int)cnt ? tie[lane] : 0u;
+  uint64_t live = cnt >= 64u ? ~0ull : (1ull << cnt) - 1ull;
+#pragma unroll
+  for (int b = 16; b >= 0; --b) {
+    const uint64_t zeros = __ballot(((p >> b) & 1u) == 0u) & live;
+    const uint32_t c0 = (uint32_t)__builtin_popcountll(zeros);
+    if (need <= c0) {
+      live = zeros;
+    } else {
+      need -= c0;
+      live &= ~zeros;
+    }
+  }
+  return (int32_t)read_lane(p, live ? __builtin_ctzll(live) : 0);
+}
+
 // The cut of a register-resident row. Level 1 (key bits 31..20) was
 // histogrammed into sm.hist by the caller. Level 2 takes the next 12 bits
 // (19..8) in the same array, cleared once its level-1 search is done;
-// level 3 the last 8 bits. Each level costs one filtered pass over the
-// registers and a search by wave 0. Ties at the k-th key take two position
-// digits (rare).
+// level 3 the last 8 bits, unless the caller knows them to be zero in every
+// key (low8_zero). Each level costs one filtered pass over the registers
+// and a search. Ties at the k-th key: a class of at most 64 elements is
+// ranked by position in one pass; a larger one takes two position digits.
 template <int BS, class Src, class Sm>
-__device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint32_t k) {
+__device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint32_t k,
+                                                   bool low8_zero = false) {
+  if (tix() == 0) sm.tie_n = 0u;  // the first search's barrier publishes it
   BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
   uint32_t need = k - h.before;
   uint32_t prefix = h.bin;  // key bits 31..20
@@ -500,20 +543,24 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint3
   need -= h.before;
   prefix = (prefix << 12) | h.bin;  // bits 31..8
   if (h.cnt == need) return Cut{8, prefix, kAllPos};
-  clear_bins<256, BS>(sm.hist);
-  __syncthreads();
-  {
-    const uint32_t p = prefix;
-    const uint32_t one = opaque_one();
-    src.for_each([&](uint32_t kk, int32_t) {
-      if ((kk >> 8) == p) lds_add(&sm.hist[kk & 0xffu], one);
-    });
+  uint32_t tau = prefix << 8;  // every key of the bin, when bits 7..0 are zero
+  if (!low8_zero) {
+    clear_bins<256, BS>(sm.hist);
+    __syncthreads();
+    {
+      const uint32_t p = prefix;
+      const uint32_t one = opaque_one();
+      src.for_each([&](uint32_t kk, int32_t) {
+        if ((kk >> 8) == p) lds_add(&sm.hist[kk & 0xffu], one);
+      });
+    }
+    __syncthreads();
+    h = group_find<256, true, BS>(sm.hist, need, sm);
+    need -= h.before;
+    tau |= h.bin;
+    if (h.cnt == need) return Cut{0, tau, kAllPos};
   }
-  __syncthreads();
-  h = group_find<256, true, BS>(sm.hist, need, sm);
-  need -= h.before;
-  const uint32_t tau = (prefix << 8) | h.bin;
-  if (h.cnt == need) return Cut{0, tau, kAllPos};
+  if (h.cnt <= 64u && tau != 0u) return Cut{0, tau, small_tie_pos(src, sm, tau, h.cnt, need)};
 
   // Several elements hold exactly the key tau and only `need` of them are
   // taken: the lowest positions. Window positions are < 2^17: two ascending
@@ -1090,7 +1137,8 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
   }
-  if (__builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk) {
+  const bool transformed = __builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk;
+  if (transformed) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const uint32_t r = ck[j] - T;
@@ -1110,7 +1158,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   }
   __syncthreads();
   const CandRegSrc<kPer> src{ck, cp};
-  const Cut cut = refine_in_registers<BS>(src, fin, kk);
+  const Cut cut = refine_in_registers<BS>(src, fin, kk, transformed);
   if (cut.pos == kAllPos) {
     const uint32_t lo = cut.prefix << cut.shift;
     const uint32_t thr = lo ? lo : 1u;
@@ -1157,7 +1205,7 @@ struct RowInfo {
 };
 
 // Class of a row: short = trivial (L <= k) or span <= 8192 floats; mid =
-// span <= 16384; long = the rest.
+// span <= 16384; big = span <= 32768; long = the rest.
 __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32_t* row_starts,
                                             int32_t k, int64_t b) {
   RowInfo r;
@@ -1167,6 +1215,7 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32
   r.span = r.L + (r.s & 3);
   r.cls = (r.L <= k || r.span <= kSmallVec * 4 * kBlock) ? kClassShort
           : (r.span <= kLargeVec * 4 * kBlock)            ? kClassMid
+          : (r.span <= kBigVec * 4 * kBigBlock)           ? kClassBig
                                                           : kClassLong;
   return r;
 }
@@ -1241,6 +1290,21 @@ __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
   if (b < 0) return;
   __shared__ SmemReg sm;
   row_in_registers<kLargeVec>(row_view(p, b, r), p.k, row_emit<kPaged>(p, b), sm);
+}
+
+// Spans of 16385 .. 32768 floats, kept in registers by 512 threads (16
+// float4 each): 128 KiB of loads in flight per row. At 80 VGPRs three rows
+// share a CU, so one row's searches overlap the others' loads (two rows of
+// 1024 threads with 8 float4 each ran 10-50% slower).
+template <bool kPaged>
+__global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) void
+rows_big_kernel(const Params p) {
+  RowInfo r;
+  const int64_t b = class_row<kClassBig>(p, r);
+  if (b < 0) return;
+  __shared__ SmemRegB<kBigBlock> sm;
+  row_in_registers<kBigVec, kPaged, kBigBlock>(row_view(p, b, r), p.k, row_emit<kPaged>(p, b),
+                                               sm);
 }
 
 // Whether row b is served by the split kernel: it was planned as a split
@@ -1754,11 +1818,11 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
       zero_area(num_rows, plan, q, kPlanBlock);
     return;
   }
-  __shared__ uint32_t count[3];
-  __shared__ uint32_t fill[3];
+  __shared__ uint32_t count[kNumClasses];
+  __shared__ uint32_t fill[kNumClasses];
   __shared__ uint32_t n_split;
   __shared__ uint32_t n_items;
-  if (tix() < 3) {
+  if (tix() < kNumClasses) {
     count[tix()] = 0;
     fill[tix()] = 0;
   }
@@ -1797,7 +1861,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     slot[b] = q;
   }
   __syncthreads();
-  const uint32_t off[3] = {0u, count[0], count[0] + count[1]};
+  uint32_t off[kNumClasses];
+  off[0] = 0u;
+#pragma unroll
+  for (int c = 1; c < kNumClasses; ++c) off[c] = off[c - 1] + count[c - 1];
   int32_t* list = plan + kPlanHeaderWords;
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const int32_t c = cls[b];
@@ -1807,7 +1874,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     plan[kPlanWordMagic] = kPlanMagic;
     plan[kPlanWordRows] = num_rows;
     plan[kPlanWordK] = k;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < kNumClasses; ++c) {
       plan[kPlanWordCount + c] = (int32_t)count[c];
       plan[kPlanWordOffset + c] = (int32_t)off[c];
     }
@@ -1864,7 +1931,8 @@ int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
   const dim3 block(kBlock);
   const bool mid = p.stride > (int64_t)kSmallVec * 4 * kBlock;
-  const bool lng = p.stride > (int64_t)kLargeVec * 4 * kBlock;
+  const bool big = p.stride > (int64_t)kLargeVec * 4 * kBlock;
+  const bool lng = p.stride > (int64_t)kBigVec * 4 * kBigBlock;
   if (!lng) p.plan = nullptr;
   if (lng && p.plan) {
     const dim3 items((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg));
@@ -1877,6 +1945,7 @@ int launch_rows(Params p, hipStream_t stream) {
     hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
   }
   if (mid) hipLaunchKernelGGL((rows_mid_kernel<kPaged>), grid, block, 0, stream, p);
+  if (big) hipLaunchKernelGGL((rows_big_kernel<kPaged>), grid, dim3(kBigBlock), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }
 

@@ -93,6 +93,26 @@ def test_edge_batch(orc, mode, k, use_plan):
     check(orc, p, use_plan=use_plan, with_raw=not use_plan)
 
 
+def _tie_rows(k):
+    rows = []
+    for L in (3000, 12000, 30000, 60000, 131072):
+        for tied, need in ((64, 1), (64, 37), (64, 63), (65, 40), (2, 1), (33, 17), (200, 150)):
+            if need <= k and k - need + tied <= L:
+                rows.append((L, L % 4, ("ties", k - need, tied)))
+    return rows
+
+
+@pytest.mark.parametrize("use_plan", [False, True])
+@pytest.mark.parametrize("mode", ["ragged", "paged"])
+@pytest.mark.parametrize("k", [2048, 100])
+def test_tie_class_sizes(orc, mode, k, use_plan):
+    """The k-th key shared by 2 to 200 elements, of which 1 to 150 are
+    taken (lowest positions first): tie classes of at most 64 elements and
+    larger ones, on every row length class."""
+    p = edge_batch(3000 + k, mode, k, _tie_rows(k), name=f"ties_{mode}_k{k}")
+    check(orc, p, use_plan=use_plan, with_raw=not use_plan)
+
+
 def _plan_words(plan):
     return plan.cpu().numpy().view(np.int32)
 

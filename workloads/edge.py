@@ -16,7 +16,23 @@ PATTERNS = ("normal", "fp16", "alphabet", "equal", "neg_inf", "increasing", "dec
 _ALPHABET = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.0, np.inf], dtype=np.float32)
 
 
-def _values(rng, pattern: str, L: int) -> np.ndarray:
+def _tie_class(rng, L: int, above: int, tied: int) -> np.ndarray:
+    """``above`` elements at 10, ``tied`` at 5 (distinct random positions),
+    the rest uniform in (-1, 1): for above < k < above + tied the k-th key is
+    shared by ``tied`` elements, of which k - above are taken."""
+    v = rng.uniform(-1.0, 1.0, size=L).astype(np.float32)
+    idx = rng.permutation(L)[:above + tied]
+    v[idx[:above]] = 10.0
+    v[idx[above:]] = 5.0
+    return v
+
+
+def _values(rng, pattern, L: int) -> np.ndarray:
+    """``pattern`` is a name from PATTERNS or ("ties", above, tied)."""
+    if isinstance(pattern, tuple):
+        kind, above, tied = pattern
+        assert kind == "ties" and above + tied <= L
+        return _tie_class(rng, L, above, tied)
     if pattern == "normal":
         return rng.standard_normal(L, dtype=np.float32)
     if pattern == "fp16":
