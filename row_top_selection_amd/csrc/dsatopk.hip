@@ -240,12 +240,23 @@ constexpr int kLongBlock = 1024;
 // in random order the list is compacted a handful of times per row.
 constexpr int kS1Chunk = 4 * kLongBlock;
 constexpr int kS1Depth = 4;
-constexpr int kS1Cap = 8176;
+constexpr int kS1Cap = 8160;
 
+// The list's length lives in registers, never in one shared counter that
+// a fast wave could bump for the next chunk before a slow wave has read it
+// for this one. Chunk c takes slots from ccnt[c % 4], which holds only that
+// chunk's appends: after the chunk's barrier every wave adds it to its
+// length, and thread 0 zeroes the counter of chunk c - 2 (read by everyone
+// before the barrier of chunk c - 1, next used by chunk c + 2 after the
+// barrier of chunk c + 1). A compaction ranks its kept pairs by per-wave
+// counts in wcnt; the warm start, which appends once between barriers,
+// counts in n0.
 struct SmemS1 {
   uint2 cand[kS1Cap];
   uint32_t hist[kBins];
-  uint32_t n;  // candidates in cand
+  uint32_t wcnt[kLongBlock / 64];
+  uint32_t ccnt[4];
+  uint32_t n0;
   uint32_t bcast[4];
 };
 
@@ -864,6 +875,16 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
 // cut (ties included) and emits. Returns false, having written nothing,
 // when ties keep the list too full to take another chunk; the caller then
 // runs the two-pass path.
+// From per-wave counts cnt[0 .. W) (written before a barrier the caller
+// has passed): x = the count of the waves before this one, y = the total.
+template <int W>
+__device__ __forceinline__ uint2 wave_slots(const uint32_t* cnt) {
+  const uint32_t c = lane_id() < W ? cnt[lane_id()] : 0u;
+  const uint32_t inc = wave_inclusive_sum(c);
+  const int w = wave_id();
+  return make_uint2(w ? read_lane(inc, w - 1) : 0u, read_lane(inc, W - 1));
+}
+
 template <int BS>
 __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint32_t& T,
                                                    uint32_t& n) {
@@ -895,21 +916,17 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
   }
   constexpr int kPer = (kS1Cap + BS - 1) / BS;
   uint2 mine[kPer];
+  uint32_t total = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint32_t i = (uint32_t)(j * BS + t);
     mine[j] = i < n ? sm.cand[i] : make_uint2(0u, 0u);
+    total += (uint32_t)__builtin_popcountll(__ballot(mine[j].x >= Tn));
   }
-  __syncthreads();
-  if (t == 0) sm.n = 0;
-  __syncthreads();
-  // one LDS atomic per wave for all of its kept pairs
-  uint32_t total = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) total += (uint32_t)__builtin_popcountll(__ballot(mine[j].x >= Tn));
-  uint32_t base = 0;
-  if (lane_id() == 0 && total) base = atomicAdd(&sm.n, total);
-  base = read_lane(base, 0);
+  if (lane_id() == 0) sm.wcnt[wave_id()] = total;
+  __syncthreads();  // counts written, and every pair is in registers
+  const uint2 st = wave_slots<BS / 64>(sm.wcnt);
+  uint32_t base = st.x;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const bool keep = mine[j].x >= Tn;
@@ -919,8 +936,7 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
     if (keep) sm.cand[base + rank] = mine[j];
     base += (uint32_t)__builtin_popcountll(m);
   }
-  __syncthreads();
-  n = __builtin_amdgcn_readfirstlane(sm.n);
+  n = st.y;
   T = Tn;
   return n + (uint32_t)kS1Chunk <= (uint32_t)kS1Cap;
 }
@@ -934,8 +950,9 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   const int32_t nchunk = (nvec + BS - 1) / BS;
   const __amdgpu_buffer_rsrc_t rs = row_buffer(rv.base4, nvec);
   const int32_t off = t * 16;
+  if (t < 4) sm.ccnt[t] = 0;
   if (t == 0) {
-    sm.n = 0;
+    sm.n0 = 0;
     sm.bcast[3] = 0;  // the final cut's count of saturated offsets
   }
   uint32_t T = 1;
@@ -945,9 +962,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, c * BS * 16,
                                                                          kStreamingLoad));
   };
-  // Pairs (key[q], a0 + q - rem) with sel[q] to the list: one LDS atomic
-  // per wave for the four.
-  auto append4 = [&](const uint32_t (&key)[4], const bool (&sel)[4], int32_t a0) {
+  // Chunk c's pairs (key[q], a0 + q - rem) with sel[q] to the list after
+  // position n: one ccnt[c % 4] atomic per wave for the four, then the
+  // chunk's barrier, after which n is the new length in every wave.
+  auto append4 = [&](const uint32_t (&key)[4], const bool (&sel)[4], int32_t a0, int c4) {
     uint64_t m[4];
     uint32_t total = 0;
 #pragma unroll
@@ -957,8 +975,8 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     }
     if (total) {
       uint32_t base = 0;
-      if (lane_id() == 0) base = atomicAdd(&sm.n, total);
-      base = read_lane(base, 0);
+      if (lane_id() == 0) base = atomicAdd(&sm.ccnt[c4], total);
+      base = n + read_lane(base, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
@@ -967,9 +985,14 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         base += (uint32_t)__builtin_popcountll(m[q]);
       }
     }
+    __syncthreads();
+    n += __builtin_amdgcn_readfirstlane(sm.ccnt[c4]);
+    if (tix() == 0) sm.ccnt[(c4 + 2) & 3] = 0;
   };
-  // The warm-start subset's pairs that `sel` takes, to the list: one LDS
-  // atomic per wave for all of them.
+  // The warm-start subset's pairs that `sel` takes open the list: one
+  // n0 atomic per wave and half, lane masks in scalar registers; then the
+  // barrier that ends the step (the caller has made sure that nothing reads
+  // the aliased final-cut space any more).
   auto append_all = [&](const uint32_t (&wk)[kS1Depth][4], auto sel) {
     const uint64_t below = (1ull << lane_id()) - 1ull;  // lanes under this one
     constexpr int kHalf = kS1Depth / 2;  // two batches: fewer live lane masks
@@ -986,7 +1009,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
           total += (uint32_t)__builtin_popcountll(m[e][q]);
         }
       uint32_t base = 0;
-      if (lane_id() == 0 && total) base = atomicAdd(&sm.n, total);
+      if (lane_id() == 0 && total) base = atomicAdd(&sm.n0, total);
       base = read_lane(base, 0);
 #pragma unroll
       for (int e = 0; e < kHalf; ++e)
@@ -1000,6 +1023,8 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
           base += (uint32_t)__builtin_popcountll(mm);
         }
     }
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(sm.n0);
   };
 #pragma unroll
   for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
@@ -1039,18 +1064,14 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     const BinHit h = group_find<kBins, true, BS>(fin.hist, (uint32_t)k, fin);
     uint32_t tau;
     if (h.before + h.cnt <= (uint32_t)(kS1Cap - kS1Chunk)) {
-      __syncthreads();  // fin aliases the list
-      if (t == 0) sm.n = 0;
-      __syncthreads();
+      // the search closed with a barrier: nothing reads the final-cut space
       tau = h.bin << 20;
       tau = tau ? tau : 1u;
       append_all(wk, [tau](uint32_t kv, int32_t) { return kv >= tau; });
     } else {
       const RegSrc<kS1Depth, BS> src{wk, -rv.rem, kS1Depth - 1};
       const Cut cut = refine_in_registers<BS>(src, fin, (uint32_t)k);
-      __syncthreads();  // fin aliases the list
-      if (t == 0) sm.n = 0;
-      __syncthreads();
+      __syncthreads();  // the final-cut space aliases the list
       if (cut.pos == kAllPos) {
         const uint32_t lo = cut.prefix << cut.shift;
         tau = lo ? lo : 1u;
@@ -1063,8 +1084,6 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         });
       }
     }
-    __syncthreads();
-    n = __builtin_amdgcn_readfirstlane(sm.n);
     T = tau > 1u ? tau : 1u;
   }
   // Set when a compaction cannot make room for a chunk (heavy ties): the
@@ -1092,12 +1111,11 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         key[q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
         sel[q] = key[q] >= Tc;
       }
-      append4(key, sel, a0);
-      __syncthreads();
-      n = __builtin_amdgcn_readfirstlane(sm.n);
+      append4(key, sel, a0, d);  // c0 is a multiple of 4: c % 4 == d
       issue(buf[d], c + kS1Depth);
     }
   }
+  __syncthreads();  // every wave's last pairs are in the list
   if (overflow) return false;
 
   // The list to registers (key 0 pads: below every threshold, counted in
@@ -1107,7 +1125,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   int32_t cp[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const uint32_t i = (uint32_t)(j * BS + t);
+    const uint32_t i = (uint32_t)(j * BS + tix());
     const uint2 e = i < n ? sm.cand[i] : make_uint2(0u, 0xffffffffu);
     ck[j] = e.x;
     cp[j] = (int32_t)e.y;
@@ -1132,7 +1150,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
   int32_t* stage = reinterpret_cast<int32_t*>(fin.hist);
   if (kk == 0) {
-    for (int32_t i = t; i < k; i += BS) stage[i] = -1;
+    for (int32_t i = tix(); i < k; i += BS) stage[i] = -1;
     __syncthreads();
     write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
@@ -1174,7 +1192,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         },
         kk, stage, fin);
   }
-  for (int32_t i = (int32_t)kk + t; i < k; i += BS) stage[i] = -1;
+  for (int32_t i = (int32_t)kk + tix(); i < k; i += BS) stage[i] = -1;
   __syncthreads();
   write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
   return true;
@@ -1220,6 +1238,16 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32
   return r;
 }
 
+// row_info of the row a whole workgroup serves, in scalar registers.
+__device__ __forceinline__ RowInfo group_row_info(const Params& p, int64_t b) {
+  RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
+  r.L = __builtin_amdgcn_readfirstlane(r.L);
+  r.s = __builtin_amdgcn_readfirstlane(r.s);
+  r.span = __builtin_amdgcn_readfirstlane(r.span);
+  r.cls = __builtin_amdgcn_readfirstlane(r.cls);
+  return r;
+}
+
 __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const RowInfo& r) {
   RowView rv;
   const int32_t rem = r.s & 3;
@@ -1245,7 +1273,7 @@ template <int kClass>
 __device__ __forceinline__ int64_t class_row(const Params& p, RowInfo& r) {
   (void)p;
   const int64_t b = blockIdx.x;
-  r = row_info(p.seq_lens, p.row_starts, p.k, b);
+  r = group_row_info(p, b);
   return r.cls == kClass ? b : -1;
 }
 
@@ -1282,29 +1310,53 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
                                                                          em, sm);
 }
 
-// Spans of 8193 .. 16384 floats, kept in registers.
+// Every row of a batch with a score stride of 8193 .. 16384 floats, in one
+// launch: 256 threads per row, holding 8 or 16 float4 each by the row's
+// span. Six rows share a CU (77 VGPRs); 512 threads with 8 float4 each
+// (three rows per CU) ran 6-12% slower on such rows.
 template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
-  RowInfo r;
-  const int64_t b = class_row<kClassMid>(p, r);
-  if (b < 0) return;
+  const int64_t b = blockIdx.x;
+  const RowInfo r = group_row_info(p, b);
+  if (r.cls != kClassShort && r.cls != kClassMid) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  if (r.L <= p.k) {
+    write_trivial(em, r.L, p.k);
+    return;
+  }
   __shared__ SmemReg sm;
-  row_in_registers<kLargeVec>(row_view(p, b, r), p.k, row_emit<kPaged>(p, b), sm);
+  const RowView rv = row_view(p, b, r);
+  if (r.span <= kSmallVec * 4 * kBlock)
+    row_in_registers<kSmallVec>(rv, p.k, em, sm);
+  else
+    row_in_registers<kLargeVec>(rv, p.k, em, sm);
 }
 
-// Spans of 16385 .. 32768 floats, kept in registers by 512 threads (16
-// float4 each): 128 KiB of loads in flight per row. At 80 VGPRs three rows
-// share a CU, so one row's searches overlap the others' loads (two rows of
-// 1024 threads with 8 float4 each ran 10-50% slower).
+// Every row up to 32768 floats of a batch with a score stride above 16384
+// floats, in one launch (a launch for a class with no rows in the batch
+// still costs several microseconds): 512 threads per row, holding 4, 8 or
+// 16 float4 each by the row's span. At 80 VGPRs three rows share a CU, so
+// one row's searches overlap the others' loads (for spans above 16384, two
+// rows of 1024 threads with 8 float4 each ran 10-50% slower).
 template <bool kPaged>
 __global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) void
-rows_big_kernel(const Params p) {
-  RowInfo r;
-  const int64_t b = class_row<kClassBig>(p, r);
-  if (b < 0) return;
+rows_reg_kernel(const Params p) {
+  const int64_t b = blockIdx.x;
+  const RowInfo r = group_row_info(p, b);
+  if (r.cls == kClassLong) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  if (r.L <= p.k) {
+    write_trivial<kPaged, kBigBlock>(em, r.L, p.k);
+    return;
+  }
   __shared__ SmemRegB<kBigBlock> sm;
-  row_in_registers<kBigVec, kPaged, kBigBlock>(row_view(p, b, r), p.k, row_emit<kPaged>(p, b),
-                                               sm);
+  const RowView rv = row_view(p, b, r);
+  if (r.span <= kBigVec * kBigBlock)
+    row_in_registers<kBigVec / 4, kPaged, kBigBlock>(rv, p.k, em, sm);
+  else if (r.span <= kBigVec * 2 * kBigBlock)
+    row_in_registers<kBigVec / 2, kPaged, kBigBlock>(rv, p.k, em, sm);
+  else
+    row_in_registers<kBigVec, kPaged, kBigBlock>(rv, p.k, em, sm);
 }
 
 // Whether row b is served by the split kernel: it was planned as a split
@@ -1322,7 +1374,7 @@ template <bool kPaged>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
 rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
-  const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
+  const RowInfo r = group_row_info(p, b);
   if (r.cls != kClassLong || split_served(p, b, r)) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b);
   if (r.L <= p.k) {
@@ -1922,30 +1974,41 @@ int check_common(const float* scores, int64_t score_stride, const int32_t* seq_l
 // than about two per CU, per-row latency sets the time.
 constexpr int32_t kWideRows = 512;
 
-// Launch the class kernels the score stride allows (a row's span never
-// exceeds score_stride). The plan's row lists are used only when every
-// class is launched: a row whose class changed since planning then still
-// reaches the long-row launch.
+struct KernelLaunch {
+  void (*fn)(Params);
+  dim3 grid;
+  dim3 block;
+};
+
+// The kernels the score stride allows (a row's span never exceeds
+// score_stride), in stream order. A stride up to 8192 floats: every row is
+// short, and the short-row kernel serves the batch alone; up to 16384, the
+// mid kernel alone. Longer strides: one register kernel for every row up
+// to 32768 floats, and above that the streaming kernel for long rows and,
+// with a plan, the split kernel. Each kernel serves the rows of its own
+// classes and skips the others.
 template <bool kPaged>
 int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
-  const dim3 block(kBlock);
-  const bool mid = p.stride > (int64_t)kSmallVec * 4 * kBlock;
-  const bool big = p.stride > (int64_t)kLargeVec * 4 * kBlock;
   const bool lng = p.stride > (int64_t)kBigVec * 4 * kBigBlock;
   if (!lng) p.plan = nullptr;
-  if (lng && p.plan) {
-    const dim3 items((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg));
-    hipLaunchKernelGGL((rows_split_kernel<kPaged>), items, block, 0, stream, p);
-  }
-  if (lng) hipLaunchKernelGGL((rows_long_kernel<kPaged>), grid, dim3(kLongBlock), 0, stream, p);
-  if (p.num_rows <= kWideRows) {
-    hipLaunchKernelGGL((rows_wide_kernel<kPaged>), grid, dim3(kWideBlock), 0, stream, p);
+  KernelLaunch ls[3];
+  int n = 0;
+  if (p.stride <= (int64_t)kSmallVec * 4 * kBlock) {
+    if (p.num_rows <= kWideRows)
+      ls[n++] = {rows_wide_kernel<kPaged>, grid, dim3(kWideBlock)};
+    else
+      ls[n++] = {rows_short_kernel<kPaged>, grid, dim3(kBlock)};
+  } else if (p.stride <= (int64_t)kLargeVec * 4 * kBlock) {
+    ls[n++] = {rows_mid_kernel<kPaged>, grid, dim3(kBlock)};
   } else {
-    hipLaunchKernelGGL((rows_short_kernel<kPaged>), grid, block, 0, stream, p);
+    if (lng && p.plan)
+      ls[n++] = {rows_split_kernel<kPaged>,
+                 dim3((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg)), dim3(kBlock)};
+    if (lng) ls[n++] = {rows_long_kernel<kPaged>, grid, dim3(kLongBlock)};
+    ls[n++] = {rows_reg_kernel<kPaged>, grid, dim3(kBigBlock)};
   }
-  if (mid) hipLaunchKernelGGL((rows_mid_kernel<kPaged>), grid, block, 0, stream, p);
-  if (big) hipLaunchKernelGGL((rows_big_kernel<kPaged>), grid, dim3(kBigBlock), 0, stream, p);
+  for (int i = 0; i < n; ++i) ls[i].fn<<<ls[i].grid, ls[i].block, 0, stream>>>(p);
   return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
 }
 

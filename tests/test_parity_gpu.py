@@ -270,3 +270,29 @@ def test_many_long_rows_are_streamed(orc):
     got, ok = gpu_run.run(p, d, use_plan=True)
     assert ok
     assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
+
+
+@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_long_x2048"])
+def test_sustained_launch_sampled_rows(orc, name):
+    """The launches the benchmark times for its sustained figures (about
+    1 GiB of scores: every CU serves several rounds of rows, and the waves
+    of a workgroup drift furthest apart), three times with the plan; 40
+    sampled rows against the oracle after each."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.scaled_decode(32768) if name.startswith("paged_decode") else \
+        workloads.scaled_long(2048)
+    print(f"[gpu] {name} sustained launch", flush=True)
+    d = gpu_run.to_dev(p)
+    rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, p.num_rows - 1, 36)
+                                     .astype(np.int64)]))
+    want = orc.paged(p.scores[rows], p.seq_lens[rows], None, p.page_table[rows], p.page_size,
+                     p.k)
+    plan = dt.plan(d["lens"], p.k)
+    idx = torch.from_numpy(rows).to(d["scores"].device)
+    for it in range(3):
+        out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+        got = out[idx].cpu().numpy()
+        assert_rows_equal(canonical(got, p.seq_lens[rows], p.k), want, f"{name} run {it}")
