@@ -272,18 +272,20 @@ def test_many_long_rows_are_streamed(orc):
     assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
 
 
-@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_long_x2048"])
+@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_long_x2048", "paged_long_x256"])
 def test_sustained_launch_sampled_rows(orc, name):
     """The launches the benchmark times for its sustained figures (about
     1 GiB of scores: every CU serves several rounds of rows, and the waves
-    of a workgroup drift furthest apart), three times with the plan; 40
-    sampled rows against the oracle after each."""
+    of a workgroup drift furthest apart), and the largest split batch (256
+    long rows, 4096 segments), three times with the plan; 40 sampled rows
+    against the oracle after each."""
     import torch
 
     import row_top_selection_amd as dt
 
-    p = workloads.scaled_decode(32768) if name.startswith("paged_decode") else \
-        workloads.scaled_long(2048)
+    rows_of = {"paged_decode_x32768": 32768, "paged_long_x2048": 2048, "paged_long_x256": 256}
+    n = rows_of[name]
+    p = workloads.scaled_decode(n) if name.startswith("paged_decode") else workloads.scaled_long(n)
     print(f"[gpu] {name} sustained launch", flush=True)
     d = gpu_run.to_dev(p)
     rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, p.num_rows - 1, 36)
@@ -296,3 +298,6 @@ def test_sustained_launch_sampled_rows(orc, name):
         out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
         got = out[idx].cpu().numpy()
         assert_rows_equal(canonical(got, p.seq_lens[rows], p.k), want, f"{name} run {it}")
+    words = _plan_words(plan)
+    assert words[14] == 0, "a segment timed out waiting for its row"
+    assert (words[12] == n) == (n <= SPLIT_CAP)
