@@ -249,14 +249,15 @@ constexpr int kS1Cap = 8160;
 // length, and thread 0 zeroes the counter of chunk c - 2 (read by everyone
 // before the barrier of chunk c - 1, next used by chunk c + 2 after the
 // barrier of chunk c + 1). A compaction ranks its kept pairs by per-wave
-// counts in wcnt; the warm start, which appends once between barriers,
-// counts in n0.
+// counts in wave_cnt; the warm start, which appends once between barriers,
+// counts in n0. After the last chunk the final cut reads the list in place.
 struct SmemS1 {
   uint2 cand[kS1Cap];
-  uint32_t hist[kBins];
-  uint32_t wcnt[kLongBlock / 64];
+  uint32_t hist[kBins];                 // digit histograms; finally the output stage
+  uint32_t wave_cnt[kLongBlock / 64];   // per-wave counts (compaction, stage)
   uint32_t ccnt[4];
   uint32_t n0;
+  uint32_t tie_n;
   uint32_t bcast[4];
 };
 
@@ -354,6 +355,34 @@ struct CandRegSrc {
   __device__ __forceinline__ void for_each(F&& f) const {
 #pragma unroll
     for (int j = 0; j < NP; ++j) f(key[j], pos[j]);
+  }
+};
+
+// The (key, position) pairs of a streamed row's LDS list, as they stand:
+// thread t takes entries t, t + BS, ... . With `offsets` the key is the
+// pair's offset above T, min(key - T, 2^24 - 2) + 1, moved to bits 31..8:
+// the pairs just above T spread over the digits, and every offset that
+// reaches the bound compares above all the others.
+template <int BS>
+struct ListSrc {
+  const uint2* cand;
+  uint32_t n;
+  uint32_t T;
+  bool offsets;
+
+  static constexpr uint32_t kSat = (1u << 24) - 2u;
+
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    for (uint32_t i = (uint32_t)tix(); i < n; i += BS) {
+      const uint2 e = cand[i];
+      uint32_t key = e.x;
+      if (offsets) {
+        const uint32_t r = key - T;
+        key = ((r < kSat ? r : kSat) + 1u) << 8;
+      }
+      f(key, (int32_t)e.y);
+    }
   }
 };
 
@@ -480,9 +509,20 @@ __device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t 
   return h;
 }
 
+// Whether a shared-memory layout holds the running sums of an all-wave
+// search (the 1024-thread register-row layouts do).
+template <class Sm>
+struct HasWaveSums {
+  static constexpr bool value = false;
+};
+template <int BS>
+struct HasWaveSums<SmemRegB<BS>> {
+  static constexpr bool value = BS > kBlock;
+};
+
 template <int NB, bool kDesc, int BS, class Sm>
 __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, Sm& sm) {
-  if constexpr (BS > kBlock && NB >= 4 * BS)
+  if constexpr (BS > kBlock && NB >= 4 * BS && HasWaveSums<Sm>::value)
     return all_waves_find<NB, kDesc, BS>(hist, need, sm);
   else
     return wave0_find<NB, kDesc>(hist, need, sm);
@@ -923,9 +963,9 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
     mine[j] = i < n ? sm.cand[i] : make_uint2(0u, 0u);
     total += (uint32_t)__builtin_popcountll(__ballot(mine[j].x >= Tn));
   }
-  if (lane_id() == 0) sm.wcnt[wave_id()] = total;
+  if (lane_id() == 0) sm.wave_cnt[wave_id()] = total;
   __syncthreads();  // counts written, and every pair is in registers
-  const uint2 st = wave_slots<BS / 64>(sm.wcnt);
+  const uint2 st = wave_slots<BS / 64>(sm.wave_cnt);
   uint32_t base = st.x;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -1118,70 +1158,42 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   __syncthreads();  // every wave's last pairs are in the list
   if (overflow) return false;
 
-  // The list to registers (key 0 pads: below every threshold, counted in
-  // bin 0 by every pass alike), then the register path's cut and emit.
-  constexpr int kPer = (kS1Cap + BS - 1) / BS;
-  uint32_t ck[kPer];
-  int32_t cp[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const uint32_t i = (uint32_t)(j * BS + tix());
-    const uint2 e = i < n ? sm.cand[i] : make_uint2(0u, 0xffffffffu);
-    ck[j] = e.x;
-    cp[j] = (int32_t)e.y;
-  }
-  // Offsets above T spread where the keys bunch (see the compaction): when
-  // fewer than the k taken pairs sit 2^24 - 2 or more above T, the cut
-  // runs on (min(key - T, 2^24 - 2) + 1) << 8, exact below that bound and
-  // above the pads' 0, so every saturated pair lies above the cut and is
-  // taken. The count goes through a word the final phase's LDS does not
-  // overlay.
-  constexpr uint32_t kSat = (1u << 24) - 2u;
+  // The cut and the stage run on the list where it stands. On offsets above
+  // T when fewer than the kk taken pairs reach the offset bound (those are
+  // then all above the cut, where their order does not matter); on the keys
+  // themselves otherwise.
+  const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
   {
     uint32_t sat = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      sat += (uint32_t)__builtin_popcountll(__ballot((ck[j] != 0u) & (ck[j] - T >= kSat)));
+    for (uint32_t i = (uint32_t)tix(); i < n; i += BS)
+      sat += (uint32_t)__builtin_popcountll(
+          __ballot(sm.cand[i].x - T >= ListSrc<BS>::kSat));
     if (lane_id() == 0 && sat) atomicAdd(&sm.bcast[3], sat);
   }
-  __syncthreads();  // fin aliases the list
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
   // fewer than k pairs only if the window holds keys below every
   // threshold, i.e. all-ones NaNs
-  const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
-  int32_t* stage = reinterpret_cast<int32_t*>(fin.hist);
   if (kk == 0) {
     for (int32_t i = tix(); i < k; i += BS) stage[i] = -1;
     __syncthreads();
     write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
     return true;
   }
-  const bool transformed = __builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk;
-  if (transformed) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t r = ck[j] - T;
-      ck[j] = ck[j] ? ((r < kSat ? r : kSat) + 1u) << 8 : 0u;
-    }
-  }
-  clear_bins<kBins, BS>(fin.hist);
-  __syncthreads();
+  const bool offsets = __builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk;
+  const ListSrc<BS> src{sm.cand, n, T, offsets};
   {
-    // Pads stay out of the count: they sit below every pair (which holds
-    // at least kk), so the search from the top never reaches them, and
-    // thousands of same-bin LDS atomics would serialize.
     const uint32_t one = opaque_one();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (ck[j]) lds_add(&fin.hist[ck[j] >> 20], one);
+    src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
   }
   __syncthreads();
-  const CandRegSrc<kPer> src{ck, cp};
-  const Cut cut = refine_in_registers<BS>(src, fin, kk, transformed);
+  const Cut cut = refine_in_registers<BS>(src, sm, kk, offsets);
   if (cut.pos == kAllPos) {
     const uint32_t lo = cut.prefix << cut.shift;
     const uint32_t thr = lo ? lo : 1u;
     stage_selected<BS, false>(
-        src, [thr](uint32_t kv, int32_t) { return kv >= thr; }, kk, stage, fin);
+        src, [thr](uint32_t kv, int32_t) { return kv >= thr; }, kk, stage, sm);
   } else {
     const uint32_t tau = cut.prefix;
     const int32_t pos = cut.pos;
@@ -1190,7 +1202,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         [tau, pos](uint32_t kv, int32_t j) {
           return (kv != 0u) & ((kv > tau) | ((kv == tau) & (j <= pos)));
         },
-        kk, stage, fin);
+        kk, stage, sm);
   }
   for (int32_t i = (int32_t)kk + tix(); i < k; i += BS) stage[i] = -1;
   __syncthreads();
