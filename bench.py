@@ -318,10 +318,17 @@ def main(argv=None):
     del r
     torch.cuda.empty_cache()
     if not args.quick:
+        # paged decode rows from 8192 to 131072 columns, 1 GiB of scores per
+        # launch (the decode and long-context shapes, and three between)
         sus = {}
         for name, mk in (("paged_decode_x32768", lambda: workloads.scaled_decode(32768)),
+                         ("paged_L16384_x16384", lambda: workloads.scaled_paged(16384, 16384)),
+                         ("paged_L32768_x8192", lambda: workloads.scaled_paged(32768, 8192)),
+                         ("paged_L65536_x4096", lambda: workloads.scaled_paged(65536, 4096)),
                          ("paged_long_x2048", lambda: workloads.scaled_long(2048))):
-            sus[name] = measure_workload(mk(), 20)
+            res = measure_workload(mk(), 20)
+            res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
+            sus[name] = res
             torch.cuda.empty_cache()
         line["sustained"] = sus
         wl = {}

@@ -1034,7 +1034,6 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // barrier that ends the step (the caller has made sure that nothing reads
   // the aliased final-cut space any more).
   auto append_all = [&](const uint32_t (&wk)[kS1Depth][4], auto sel) {
-    const uint64_t below = (1ull << lane_id()) - 1ull;  // lanes under this one
     constexpr int kHalf = kS1Depth / 2;  // two batches: fewer live lane masks
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1057,8 +1056,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         for (int q = 0; q < 4; ++q) {
           const int d = h * kHalf + e;
           const uint64_t mm = m[e][q];
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
           if ((mm >> lane_id()) & 1ull)
-            sm.cand[base + (uint32_t)__builtin_popcountll(mm & below)] =
+            sm.cand[base + rank] =
                 make_uint2(wk[d][q], (uint32_t)((d * BS + t) * 4 + q - rv.rem));
           base += (uint32_t)__builtin_popcountll(mm);
         }

@@ -272,7 +272,8 @@ def test_many_long_rows_are_streamed(orc):
     assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
 
 
-@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_long_x2048", "paged_long_x256"])
+@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_L32768_x8192", "paged_L65536_x4096",
+                                  "paged_long_x2048", "paged_long_x256"])
 def test_sustained_launch_sampled_rows(orc, name):
     """The launches the benchmark times for its sustained figures (about
     1 GiB of scores: every CU serves several rounds of rows, and the waves
@@ -283,9 +284,13 @@ def test_sustained_launch_sampled_rows(orc, name):
 
     import row_top_selection_amd as dt
 
-    rows_of = {"paged_decode_x32768": 32768, "paged_long_x2048": 2048, "paged_long_x256": 256}
-    n = rows_of[name]
-    p = workloads.scaled_decode(n) if name.startswith("paged_decode") else workloads.scaled_long(n)
+    makers = {"paged_decode_x32768": lambda: workloads.scaled_decode(32768),
+              "paged_L32768_x8192": lambda: workloads.scaled_paged(32768, 8192),
+              "paged_L65536_x4096": lambda: workloads.scaled_paged(65536, 4096),
+              "paged_long_x2048": lambda: workloads.scaled_long(2048),
+              "paged_long_x256": lambda: workloads.scaled_long(256)}
+    p = makers[name]()
+    n = p.num_rows
     print(f"[gpu] {name} sustained launch", flush=True)
     d = gpu_run.to_dev(p)
     rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, p.num_rows - 1, 36)

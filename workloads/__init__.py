@@ -28,6 +28,7 @@ from .configs import (  # noqa: F401
     make_workload,
     scaled_decode,
     scaled_long,
+    scaled_paged,
     short_mix,
     random_page_tables,
 )

@@ -193,3 +193,20 @@ def scaled_long(rows: int, seed: Optional[int] = None) -> Problem:
     p = paged_long(seed, rows=rows)
     p.name = f"paged_long_x{rows}"
     return p
+
+
+def scaled_paged(L: int, rows: int, fp16: bool = False, seed: Optional[int] = None) -> Problem:
+    """PAGED decode rows of one window length ``L`` (sustained-rate runs
+    between the decode and long-context shapes): N(0,1) fp32 scores (rounded
+    to fp16 if ``fp16``), k = 2048, page size 64, each row's L / 64 table
+    entries a random permutation of 4096 (or L / 64, if more) pages."""
+    if seed is None:
+        seed = BASE_SEED + 107
+    rng = np.random.default_rng(seed)
+    seq_lens = np.full(rows, L, dtype=np.int32)
+    scores = _normal(rng, (rows, L))
+    if fp16:
+        scores = scores.astype(np.float16).astype(np.float32)
+    width = -(-L // PAGE_SIZE)
+    pt = random_page_tables(rng, rows, width, max(width, 4096))
+    return Problem(f"paged_L{L}_x{rows}", "paged", 2048, scores, seq_lens, page_table=pt)
