@@ -230,10 +230,82 @@ def cpu_baseline(p, budget_s: float = 12.0) -> dict:
     }
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_configs() -> dict:
+    """The oracle on every workload: one pass over the full batch with all
+    host threads, and one thread over the batch's first rows (at most 32)."""
+    import oracle
+
+    orc = oracle.default()
+    threads = oracle.default_threads()
+    res = {"cpu": cpu_model(), "threads": threads}
+    for name in workloads_names():
+        p = only_workload(name)
+
+        def run(sub, nthreads):
+            t0 = time.perf_counter()
+            if p.mode == "ragged":
+                orc.ragged(p.scores[sub], p.seq_lens[sub],
+                           None if p.row_starts is None else p.row_starts[sub],
+                           p.out_offsets[sub], p.k, threads=nthreads)
+            else:
+                orc.paged(p.scores[sub], p.seq_lens[sub],
+                          None if p.row_starts is None else p.row_starts[sub],
+                          p.page_table[sub], p.page_size, p.k, threads=nthreads)
+            return time.perf_counter() - t0
+
+        full = slice(0, p.num_rows)
+        head = slice(0, min(p.num_rows, 32))
+        tf = run(full, threads)
+        t1 = run(head, 1)
+        L = p.window_lengths()
+        score_head = int(4 * L[head][L[head] > p.k].sum())
+        res[name] = {"rows": p.num_rows, "wall_s": tf, "rows_per_s": p.num_rows / tf,
+                     "score_GBps": algorithmic_bytes(p)["score"] / tf / 1e9,
+                     "one_thread": {"rows": head.stop, "wall_s": t1, "rows_per_s": head.stop / t1,
+                                    "score_GBps": score_head / t1 / 1e9}}
+    return res
+
+
+def workloads_names():
+    import workloads
+
+    return list(workloads.WORKLOADS)
+
+
 def describe(p) -> dict:
     L = p.window_lengths()
     return {"rows": p.num_rows, "k": p.k, "mode": p.mode,
             "seq_len": int(L[0]) if (L == L[0]).all() else [int(L.min()), int(L.max())]}
+
+
+SUSTAINED = {
+    "paged_decode_x32768": lambda w: w.scaled_decode(32768),
+    "paged_L16384_x16384": lambda w: w.scaled_paged(16384, 16384),
+    "paged_L32768_x8192": lambda w: w.scaled_paged(32768, 8192),
+    "paged_L65536_x4096": lambda w: w.scaled_paged(65536, 4096),
+    "paged_long_x2048": lambda w: w.scaled_long(2048),
+}
+
+
+def only_workload(name: str):
+    import workloads
+
+    if name in SUSTAINED:
+        return SUSTAINED[name](workloads)
+    if name == "all_trivial":
+        return workloads.all_trivial()
+    return workloads.make_workload(name)
 
 
 def measure_workload(p, iters: int) -> dict:
@@ -256,6 +328,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB (counter calibration)")
+    ap.add_argument("--only", default=None,
+                    help="only replay one workload's transform --steps times (counter runs): "
+                         "a workload name, a sustained name, or all_trivial")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the selection shards by rows with no exchange, "
@@ -274,6 +349,15 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_CALIBRATION_BYTES, "launches": 5}), flush=True)
+        return 0
+    if args.only:
+        p = only_workload(args.only)
+        r = Runner(p)
+        for i in range(args.steps):
+            r.transform(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.only, "launches": args.steps,
+                          "bytes_per_launch": algorithmic_bytes(p)}), flush=True)
         return 0
     p = workloads.make_workload("paged_decode")
     r = Runner(p)
@@ -321,12 +405,8 @@ def main(argv=None):
         # paged decode rows from 8192 to 131072 columns, 1 GiB of scores per
         # launch (the decode and long-context shapes, and three between)
         sus = {}
-        for name, mk in (("paged_decode_x32768", lambda: workloads.scaled_decode(32768)),
-                         ("paged_L16384_x16384", lambda: workloads.scaled_paged(16384, 16384)),
-                         ("paged_L32768_x8192", lambda: workloads.scaled_paged(32768, 8192)),
-                         ("paged_L65536_x4096", lambda: workloads.scaled_paged(65536, 4096)),
-                         ("paged_long_x2048", lambda: workloads.scaled_long(2048))):
-            res = measure_workload(mk(), 20)
+        for name, mk in SUSTAINED.items():
+            res = measure_workload(mk(workloads), 20)
             res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
             sus[name] = res
             torch.cuda.empty_cache()
@@ -337,6 +417,8 @@ def main(argv=None):
             torch.cuda.empty_cache()
         line["workloads"] = wl
     line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+    if not args.quick:
+        line["cpu_configs"] = cpu_configs()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -22,6 +22,7 @@ Every generator uses ``numpy.random.default_rng(seed)`` and draws in the
 fixed order seq_lens, scores, page tables, pinned rows.
 """
 from .configs import (  # noqa: F401
+    all_trivial,
     BASE_SEED,
     WORKLOADS,
     Problem,

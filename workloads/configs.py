@@ -210,3 +210,17 @@ def scaled_paged(L: int, rows: int, fp16: bool = False, seed: Optional[int] = No
     width = -(-L // PAGE_SIZE)
     pt = random_page_tables(rng, rows, width, max(width, 4096))
     return Problem(f"paged_L{L}_x{rows}", "paged", 2048, scores, seq_lens, page_table=pt)
+
+
+def all_trivial(seed: Optional[int] = None) -> Problem:
+    """128 PAGED rows whose windows all fit in k (L uniform in [1, 2048],
+    k = 2048): every row takes the trivial path, so a launch should read no
+    scores at all (a counter check)."""
+    if seed is None:
+        seed = BASE_SEED + 109
+    rng = np.random.default_rng(seed)
+    R = 128
+    seq_lens = rng.integers(1, 2049, size=R).astype(np.int32)
+    scores = _normal(rng, (R, 8192))
+    pt = random_page_tables(rng, R, 128, 4096)
+    return Problem("all_trivial", "paged", 2048, scores, seq_lens, page_table=pt)
