@@ -12,6 +12,8 @@ only builds that file with gcc, marshals numpy arrays to it, and exposes:
 - :func:`select`  - selected window positions, ascending, then -1 padding
 - :func:`ragged`  - RAGGED outputs (position + out_offset), same layout
 - :func:`paged`   - PAGED outputs (page-table mapped), valid slots sorted
+- ``Oracle.paged_packed`` - packed PAGED outputs (a table-row map and table
+  starts per row), valid slots sorted
 
 All results are int32 ``[num_rows, k]`` with the valid slots first.
 """
@@ -60,6 +62,9 @@ class Oracle:
         lib.oracle_emit_paged.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P,
                                           ctypes.c_int64, ctypes.c_int32, P]
         lib.oracle_emit_paged.restype = ctypes.c_int
+        lib.oracle_emit_paged_packed.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P,
+                                                 ctypes.c_int64, ctypes.c_int32, P, P, P]
+        lib.oracle_emit_paged_packed.restype = ctypes.c_int
         self.lib = lib
 
     def select(self, scores, seq_lens, row_starts, k, threads=None):
@@ -80,6 +85,16 @@ class Oracle:
         """PAGED outputs: ascending page-table-mapped positions, then -1."""
         return self.emit_paged(self.select(scores, seq_lens, row_starts, k, threads),
                                page_table, page_size)
+
+    def emit_paged_packed(self, sel, page_table, page_size, table_rows=None, table_starts=None):
+        return _emit_paged_packed(self.lib, sel, page_table, page_size, table_rows, table_starts)
+
+    def paged_packed(self, scores, seq_lens, row_starts, page_table, page_size, k,
+                     table_rows=None, table_starts=None, threads=None):
+        """Packed PAGED outputs: row b maps window position j through table
+        row table_rows[b] at table position table_starts[b] + j."""
+        return self.emit_paged_packed(self.select(scores, seq_lens, row_starts, k, threads),
+                                      page_table, page_size, table_rows, table_starts)
 
 
 def default() -> Oracle:
@@ -161,6 +176,32 @@ def _emit_paged(lib, sel, page_table, page_size):
                                    page_table.shape[1], int(page_size), _ptr(out))
         if rc != 0:
             raise ValueError("page_size must be a power of two >= 1")
+    return out
+
+
+def _emit_paged_packed(lib, sel, page_table, page_size, table_rows, table_starts):
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    R, k = sel.shape
+    page_table = np.ascontiguousarray(page_table, dtype=np.int32)
+    if page_table.ndim != 2:
+        raise ValueError("page_table must be [table_rows, width]")
+    T, W = page_table.shape
+    tr = None if table_rows is None else _i32(table_rows, R, "table_rows")
+    ts = None if table_starts is None else _i32(table_starts, R, "table_starts")
+    rows = tr if tr is not None else np.arange(R)
+    if R and (rows.min() < 0 or rows.max() >= T):
+        raise ValueError("table row outside the page table")
+    q_max = (0 if ts is None else ts.astype(np.int64)) + sel.max(axis=1).astype(np.int64)
+    if R and (q_max // int(page_size)).max() >= W:
+        raise ValueError("table position outside the page-table row")
+    out = np.empty_like(sel)
+    if R:
+        rc = lib.oracle_emit_paged_packed(_ptr(sel), R, k, _ptr(page_table), W, int(page_size),
+                                          _ptr(tr), _ptr(ts), _ptr(out))
+        if rc == 1:
+            raise ValueError("page_size must be a power of two >= 1")
+        if rc == 2:
+            raise ValueError("negative table position")
     return out
 
 

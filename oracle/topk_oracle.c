@@ -36,6 +36,17 @@
  *    + pos % page_size, with page_size a power of two.
  *    (PR #35175 digest, TopKProblem::transform_output / page_to_indices
  *    with page_bits = log2(page_size).)
+ *  - Packed PAGED emit: row b looks up table row table_rows[b] (b when
+ *    absent) at table position table_starts[b] + pos (pos when absent):
+ *    several query rows of one request share that request's table, and the
+ *    score window's start in the batch-wide score layout (row_start) is
+ *    separate from the window's start in the request's own table.
+ *    (sglang/FlashInfer packed PAGED digest, "fix(dsa): use FlashInfer fused
+ *    top-k for packed PAGED rows": page_table_row_starts = row_starts minus
+ *    the request's cu_seqlens_k start, gathered by row_to_batch.)
+ *  - Raw positions beside the PAGED output: the selected window positions
+ *    themselves (PR #26788 digest, the transform's optional out_raw_indices;
+ *    raw-index mode in the PR #35175 digest, "Motivation").
  *  - Comparison form: the valid outputs are compared as a sorted list,
  *    because the kernels' output order inside a row is free (the pages'
  *    test compares sets).
@@ -221,6 +232,39 @@ int oracle_emit_paged(const int32_t* sel, int32_t num_rows, int32_t k,
                 out[b * k + t] = page * page_size + (j & (page_size - 1));
                 ++n;
             }
+        }
+        qsort(out + b * k, (size_t)n, sizeof(int32_t), cmp_i32_asc);
+    }
+    return 0;
+}
+
+/*
+ * Packed PAGED emit: q = table_starts[b] + j (j when table_starts is NULL),
+ * out = page_table[tr][q >> log2(p)] * p + (q & (p - 1)) with
+ * tr = table_rows[b] (b when table_rows is NULL), -1 for padding; the valid
+ * slots are then sorted ascending. Returns 1 for a page_size that is not a
+ * power of two, 2 for a negative table position.
+ */
+int oracle_emit_paged_packed(const int32_t* sel, int32_t num_rows, int32_t k,
+                             const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                             const int32_t* table_rows, const int32_t* table_starts,
+                             int32_t* out) {
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0) return 1;
+    for (int64_t b = 0; b < num_rows; ++b) {
+        int64_t tr = table_rows ? table_rows[b] : b;
+        int64_t ts = table_starts ? table_starts[b] : 0;
+        int32_t n = 0;
+        for (int32_t t = 0; t < k; ++t) {
+            int32_t j = sel[b * k + t];
+            if (j < 0) {
+                out[b * k + t] = -1;
+                continue;
+            }
+            int64_t q = ts + j;
+            if (q < 0) return 2;
+            int64_t page = page_table[tr * pt_stride + q / page_size];
+            out[b * k + t] = (int32_t)(page * page_size + q % page_size);
+            ++n;
         }
         qsort(out + b * k, (size_t)n, sizeof(int32_t), cmp_i32_asc);
     }

@@ -255,3 +255,65 @@ def pin_invariants(orc, problem, sample_rows=None):
     outside = 1e3 if p.name == "ragged_extend" else None
     check_row_invariants(scores, lens, starts, p.k, sel, outside=outside)
     return sel
+
+
+def pin_packed_emit(orc, seed=23):
+    """Packed PAGED emit (a table-row map and per-row table starts).
+
+    - A hand case: table rows [[7, 3], [5, 9]], page size 2; row 0 uses table
+      row 0 from table position 1 and selects window positions {0, 2}:
+      positions 1 and 3 map to 7*2+1 = 15 and 3*2+1 = 7; row 1 uses table
+      row 1 from position 0 and selects {1}: 5*2+1 = 11.
+    - The identity map with zero starts reduces to the PAGED emit.
+    - Random maps and starts against a brute force that expands each table
+      row into one entry per table position (no shifts or masks).
+    - The pages' shifted packed layout: query rows of a request share its
+      table (row_to_batch by query counts) and start at its first table
+      position (score window start minus the request's KV start).
+    """
+    sel = np.array([[0, 2, -1], [1, -1, -1]], np.int32)
+    pt = np.array([[7, 3], [5, 9]], np.int32)
+    got = orc.emit_paged_packed(sel, pt, 2, table_rows=np.array([0, 1], np.int32),
+                                table_starts=np.array([1, 0], np.int32))
+    assert np.array_equal(got, np.array([[7, 15, -1], [11, -1, -1]], np.int32)), got
+
+    rng = np.random.default_rng(seed)
+    for page_size in (1, 2, 64):
+        R, k, T, W = 40, 16, 7, 12
+        sel = np.full((R, k), -1, np.int32)
+        span = W * page_size
+        for b in range(R):
+            n = int(rng.integers(0, min(k, span // 2) + 1))
+            sel[b, :n] = np.sort(rng.choice(span // 2, size=n, replace=False))
+        table = rng.integers(0, 1 << 20, size=(T, W)).astype(np.int32)
+        ident = orc.emit_paged_packed(sel, table[:1].repeat(R, 0), page_size)
+        assert np.array_equal(ident, orc.emit_paged(sel, table[:1].repeat(R, 0), page_size))
+        rows = rng.integers(0, T, size=R).astype(np.int32)
+        starts = rng.integers(0, span // 2, size=R).astype(np.int32)
+        got = orc.emit_paged_packed(sel, table, page_size, table_rows=rows, table_starts=starts)
+        for b in range(R):
+            expanded = np.repeat(table[rows[b]].astype(np.int64) * page_size, page_size) + \
+                np.tile(np.arange(page_size), W)
+            J = sel[b][sel[b] >= 0]
+            want = np.sort(expanded[starts[b] + J])
+            assert np.array_equal(got[b, :len(J)], want), (page_size, b)
+            assert (got[b, len(J):] == -1).all()
+
+    # the pages' shifted packed layout, end to end from scores
+    batch, per_row, k, p = 3, 300, 20, 4
+    q_lens = np.array([2, 1, 3])
+    cu = np.arange(batch + 1) * per_row
+    row_to_batch = np.repeat(np.arange(batch), q_lens).astype(np.int32)
+    R = len(row_to_batch)
+    row_starts = cu[:-1][row_to_batch].astype(np.int32)
+    table_starts = (row_starts - cu[:-1][row_to_batch]).astype(np.int32)
+    seq_lens = rng.integers(k + 1, per_row + 1, size=R).astype(np.int32)
+    scores = rng.standard_normal((R, batch * per_row)).astype(np.float32)
+    table = rng.integers(0, 1000, size=(batch, per_row // p)).astype(np.int32)
+    got = orc.paged_packed(scores, seq_lens, row_starts, table, p, k,
+                           table_rows=row_to_batch, table_starts=table_starts)
+    for b in range(R):
+        w = scores[b, row_starts[b]:row_starts[b] + seq_lens[b]]
+        J = np.argsort(-w, kind="stable")[:k]
+        want = np.sort(table[row_to_batch[b], J // p].astype(np.int64) * p + J % p)
+        assert np.array_equal(got[b], want), b

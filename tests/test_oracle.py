@@ -15,6 +15,10 @@ def test_hand_cases(orc):
     pins.pin_hand_cases(orc)
 
 
+def test_packed_emit(orc):
+    pins.pin_packed_emit(orc)
+
+
 def test_brute_force_tiny_rows(orc):
     pins.pin_brute_force(orc)
 

@@ -55,6 +55,18 @@ MUTANTS = {
         "    if (a->w == 0.0f && b->w == 0.0f && signbit(a->w) != signbit(b->w))\n"
         "        return signbit(a->w) ? 1 : -1;\n"
         "    if (a->w > b->w) return -1;"),
+    # packed rows read their own table row instead of the mapped one
+    "packed_table_row_ignored": (
+        "int64_t tr = table_rows ? table_rows[b] : b;",
+        "int64_t tr = b;"),
+    # packed rows' table start dropped
+    "packed_table_start_ignored": (
+        "int64_t q = ts + j;",
+        "int64_t q = j;"),
+    # table start added after the page split (in-page offset only)
+    "packed_start_in_offset_only": (
+        "int64_t page = page_table[tr * pt_stride + q / page_size];",
+        "int64_t page = page_table[tr * pt_stride + j / page_size];"),
     # the window is read one column late
     "window_shifted": (
         "e[j].w = row[j];",
@@ -70,6 +82,7 @@ def _run_pins(orc):
         ("brute_force", lambda: pins.pin_brute_force(orc, rows=300)),
         ("argmax_rounds", lambda: pins.pin_argmax_rounds(orc)),
         ("invariants_small", lambda: _emit_check(orc, "paged_small")),
+        ("packed_emit", lambda: pins.pin_packed_emit(orc)),
     ]
     for name, fn in checks:
         try:
