@@ -93,11 +93,18 @@ def algorithmic_bytes(p) -> dict:
 class Runner:
     """Device copies of one workload and a rotation of its score rows."""
 
-    def __init__(self, p, rotate: bool = True):
+    def __init__(self, p, rotate: bool = True, table_rows=None, table_starts=None,
+                 raw: bool = False):
         import torch
 
         self.p = p
         dev = torch.device("cuda")
+        # packed PAGED rows and the raw-position output (dsatopk_paged_packed)
+        self.table_rows = None if table_rows is None else torch.from_numpy(table_rows).to(dev)
+        self.table_starts = None if table_starts is None else \
+            torch.from_numpy(table_starts).to(dev)
+        self.out_raw = torch.empty((p.num_rows, p.k), dtype=torch.int32, device=dev) \
+            if raw else None
         self.scores0 = torch.from_numpy(p.scores).to(dev)
         nbytes = p.scores.nbytes
         self.copies = max(1, -(-ROTATION_BYTES // nbytes)) if rotate else 1
@@ -130,7 +137,8 @@ class Runner:
                       out=self.out)
         else:
             dt.paged(s, self.lens, self.pt, p.page_size, p.k, row_starts=self.starts,
-                     plan=self.plan, out=self.out)
+                     plan=self.plan, out=self.out, table_rows=self.table_rows,
+                     table_starts=self.table_starts, out_raw=self.out_raw)
 
     def step(self, i: int):
         self.make_plan()
@@ -308,10 +316,12 @@ def only_workload(name: str):
     return workloads.make_workload(name)
 
 
-def measure_workload(p, iters: int) -> dict:
-    r = Runner(p)
+def measure_workload(p, iters: int, **packed) -> dict:
+    r = Runner(p, **packed)
     us = kernel_time_us(r.transform, iters)
     b = algorithmic_bytes(p)
+    if packed.get("raw"):
+        b = dict(b, raw=b["out"], total=b["total"] + b["out"])
     res = dict(describe(p), transform_us=us, rows_per_s=p.num_rows / (us * 1e-6),
                score_GBps=b["score"] / (us * 1e3), total_GBps=b["total"] / (us * 1e3),
                hbm_frac=b["total"] / (us * 1e3) / HBM_PEAK_GBPS, bytes=b, rotation=r.copies)
@@ -416,6 +426,17 @@ def main(argv=None):
             wl[name] = measure_workload(workloads.make_workload(name), 50)
             torch.cuda.empty_cache()
         line["workloads"] = wl
+        # the packed PAGED layout (4 requests x 1024 query rows sharing their
+        # tables, windows from each request's first column) and the raw
+        # positions written beside the paged ones
+        pk, tr, ts = workloads.packed_paged(workloads.BASE_SEED + 111, [1024] * 4, 16385,
+                                            2048, 0)
+        line["packed"] = {
+            "packed_extend": measure_workload(pk, 20, table_rows=tr, table_starts=ts, raw=True),
+            "paged_decode_x32768_raw": measure_workload(workloads.scaled_decode(32768), 20,
+                                                        raw=True),
+        }
+        torch.cuda.empty_cache()
     line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
     if not args.quick:
         line["cpu_configs"] = cpu_configs()

@@ -152,6 +152,45 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
                   void* plan, size_t plan_bytes, int32_t* out, void* stream);
 
 /*
+ * dsatopk_paged_packed - dsatopk_paged for packed rows, with raw positions
+ * beside the paged ones.
+ *
+ * Packed rows: query rows of one request share that request's page-table
+ * row, while their score windows sit at batch-wide columns of the score
+ * buffer (sglang/FlashInfer packed PAGED digest, "fix(dsa): use FlashInfer
+ * fused top-k for packed PAGED rows": the page table's start for a row is
+ * its score window start minus the request's KV start, and a row-to-batch
+ * map picks the table row). Raw positions: the transform's optional raw
+ * index output (PR #26788 digest, out_raw_indices).
+ *
+ * Arguments as for dsatopk_paged, plus:
+ *   table_rows    int32 [num_rows] (device) or NULL: row b reads page-table
+ *                 row table_rows[b] (row b when NULL). The page table may
+ *                 then hold fewer rows than num_rows.
+ *   table_starts  int32 [num_rows] (device) or NULL: window position j of
+ *                 row b is table position table_starts[b] + j (j when
+ *                 NULL); out = table[q / page_size] * page_size +
+ *                 q % page_size with q that table position.
+ *   out_raw       int32 [num_rows, k] or NULL: when given, also written
+ *                 (all of it) with the selected window positions j, slot
+ *                 for slot with out, and -1 where out holds -1.
+ *
+ * With table_rows, table_starts and out_raw all NULL this is dsatopk_paged.
+ * Device-side preconditions (not checked): table_rows[b] names a row of the
+ * page table; 0 <= table_starts[b]; the row's table positions
+ * table_starts[b] .. table_starts[b] + seq_len_b - 1 lie inside that row
+ * (page_table_stride >= ceil((table_starts[b] + seq_len_b) / page_size)).
+ *
+ * Errors: as dsatopk_paged.
+ */
+int dsatopk_paged_packed(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                         const int32_t* row_starts, const int32_t* page_table,
+                         int64_t page_table_stride, int32_t page_size,
+                         const int32_t* table_rows, const int32_t* table_starts,
+                         int32_t num_rows, int32_t k, void* plan, size_t plan_bytes,
+                         int32_t* out, int32_t* out_raw, void* stream);
+
+/*
  * dsatopk_ragged - top-k with the RAGGED emit: out = j + out_offsets[b].
  *
  * Arguments as for dsatopk_paged, with out_offsets int32 [num_rows]

@@ -24,7 +24,7 @@ STATUS = {
 }
 
 EXPORTS = ("dsatopk_status_string", "dsatopk_plan_bytes", "dsatopk_plan", "dsatopk_paged",
-           "dsatopk_ragged")
+           "dsatopk_paged_packed", "dsatopk_ragged")
 
 
 class DsatopkError(RuntimeError):
@@ -51,6 +51,10 @@ def _lib():
         lib.dsatopk_plan.argtypes = [P, P, i32, i32, P, sz, P]
         lib.dsatopk_plan.restype = ctypes.c_int
         lib.dsatopk_paged.argtypes = [P, i64, P, P, P, i64, i32, i32, i32, P, sz, P, P]
+        lib.dsatopk_paged.restype = ctypes.c_int
+        lib.dsatopk_paged_packed.argtypes = [P, i64, P, P, P, i64, i32, P, P, i32, i32, P, sz,
+                                             P, P, P]
+        lib.dsatopk_paged_packed.restype = ctypes.c_int
         lib.dsatopk_paged.restype = ctypes.c_int
         lib.dsatopk_ragged.argtypes = [P, i64, P, P, P, i32, i32, P, sz, P, P]
         lib.dsatopk_ragged.restype = ctypes.c_int
@@ -131,22 +135,46 @@ def plan(seq_lens, k: int, row_starts=None, out=None, stream=None):
 
 
 def paged(scores, seq_lens, page_table, page_size: int, k: int, row_starts=None, plan=None,
-          out=None, stream=None):
-    """PAGED top-k: int32 ``[rows, k]`` of page-table-mapped positions."""
+          out=None, stream=None, table_rows=None, table_starts=None, out_raw=None):
+    """PAGED top-k: int32 ``[rows, k]`` of page-table-mapped positions.
+
+    Packed rows (``dsatopk_paged_packed``): ``table_rows`` picks each row's
+    page-table row, ``table_starts`` its table position of window position
+    0; ``out_raw`` (int32 ``[rows, k]``, or True to allocate one) also
+    receives the window positions, slot for slot. Returns ``out``, or
+    ``(out, out_raw)`` when ``out_raw`` is given."""
     scores = _scores(scores)
     rows = int(scores.shape[0])
     _vec_i32(seq_lens, rows, "seq_lens")
     _vec_i32(row_starts, rows, "row_starts")
-    if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.shape[0] != rows:
-        raise ValueError("page_table must be [rows, width] with contiguous columns")
+    _vec_i32(table_rows, rows, "table_rows")
+    _vec_i32(table_starts, rows, "table_starts")
+    packed = table_rows is not None or table_starts is not None or out_raw is not None
+    if page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be [table rows, width] with contiguous columns")
+    if table_rows is None and page_table.shape[0] != rows:
+        raise ValueError("page_table must have one row per score row without table_rows")
     out = _out(out, rows, int(k), scores)
-    st = _lib().dsatopk_paged(
+    if out_raw is True:
+        out_raw = _out(None, rows, int(k), scores)
+    elif out_raw is not None:
+        out_raw = _out(out_raw, rows, int(k), scores)
+    if not packed:
+        st = _lib().dsatopk_paged(
+            _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
+            page_table.stride(0), int(page_size), rows, int(k), _ptr(plan),
+            0 if plan is None else plan.numel(), _ptr(out), _stream(stream))
+        if st != 0:
+            raise DsatopkError(st, "dsatopk_paged")
+        return out
+    st = _lib().dsatopk_paged_packed(
         _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
-        page_table.stride(0), int(page_size), rows, int(k), _ptr(plan),
-        0 if plan is None else plan.numel(), _ptr(out), _stream(stream))
+        page_table.stride(0), int(page_size), _ptr(table_rows), _ptr(table_starts), rows,
+        int(k), _ptr(plan), 0 if plan is None else plan.numel(), _ptr(out), _ptr(out_raw),
+        _stream(stream))
     if st != 0:
-        raise DsatopkError(st, "dsatopk_paged")
-    return out
+        raise DsatopkError(st, "dsatopk_paged_packed")
+    return out if out_raw is None else (out, out_raw)
 
 
 def ragged(scores, seq_lens, out_offsets, k: int, row_starts=None, plan=None, out=None,

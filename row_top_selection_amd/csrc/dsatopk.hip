@@ -61,6 +61,12 @@ struct Params {
   int32_t k;
   int32_t* out;
   int32_t* plan;  // plan words (header, class lists, classes, exchange areas) or null
+  // PAGED only: row b maps window position j through page-table row
+  // table_rows[b] (b if null) at table position table_starts[b] + j (j if
+  // null), and also writes j to out_raw (if not null), slot for slot
+  const int32_t* table_rows;
+  const int32_t* table_starts;
+  int32_t* out_raw;
 };
 
 // Row classes by aligned span. A row's class is recomputed by every kernel
@@ -139,21 +145,24 @@ __host__ __device__ constexpr int32_t segments_for(int32_t span) {
 template <bool kPaged>
 struct Emit {
   int32_t* out;
-  const int32_t* pt;  // the row's page-table entries (global)
+  int32_t* out_raw;   // PAGED: also the window positions, slot for slot (or null)
+  const int32_t* pt;  // the row's page-table row (global)
+  int32_t pt_off;     // table position of window position 0 (packed rows)
   int32_t pt_first;   // first entry of the LDS copy, when staged
   int32_t page_bits;
   int32_t offset;
   bool staged;        // entries pt_first .. sit in the workgroup's LDS table
 
-  __device__ __forceinline__ int32_t map(int32_t j, int32_t page) const {
-    return (int32_t)(((uint32_t)page << page_bits) | ((uint32_t)j & ((1u << page_bits) - 1u)));
+  __device__ __forceinline__ int32_t map(int32_t q, int32_t page) const {
+    return (int32_t)(((uint32_t)page << page_bits) | ((uint32_t)q & ((1u << page_bits) - 1u)));
   }
 
   // The emitted value of window position j, with the page-table entry read
   // from global memory.
   __device__ __forceinline__ int32_t value(int32_t j) const {
     if constexpr (kPaged) {
-      return map(j, pt[j >> page_bits]);
+      const int32_t q = j + pt_off;
+      return map(q, pt[q >> page_bits]);
     } else {
       return j + offset;
     }
@@ -164,12 +173,25 @@ struct Emit {
     if constexpr (kPaged) {
       // an LDS pointer by type, so that the read is an LDS read even where
       // the compiler merges this path with the global one
-      const __attribute__((address_space(3))) int32_t* q =
+      const __attribute__((address_space(3))) int32_t* e =
           (const __attribute__((address_space(3))) int32_t*)lds;
-      return map(j, q[(j >> page_bits) - pt_first]);
+      const int32_t q = j + pt_off;
+      return map(q, e[(q >> page_bits) - pt_first]);
     } else {
       return j + offset;
     }
+  }
+
+  // Output slot t takes value v of window position j (j = -1: padding).
+  __device__ __forceinline__ void put(int32_t t, int32_t j, int32_t v) const {
+    out[t] = v;
+    if (kPaged && out_raw) out_raw[t] = j;
+  }
+
+  // Page-table entries of window positions [0, L): first entry, count.
+  __device__ __forceinline__ int2 table_span(int32_t L) const {
+    const int32_t e0 = pt_off >> page_bits;
+    return make_int2(e0, L > 0 ? ((pt_off + L - 1) >> page_bits) - e0 + 1 : 0);
   }
 
   // Stage the first ceil(L / page_size) table entries into `lds` when they
@@ -184,8 +206,8 @@ struct Emit {
     if constexpr (kPaged) {
       j0 = j0 < 0 ? 0 : j0;
       if (j1 <= j0) return;
-      const int32_t e0 = j0 >> page_bits;
-      const int32_t n = ((j1 - 1) >> page_bits) - e0 + 1;
+      const int32_t e0 = (j0 + pt_off) >> page_bits;
+      const int32_t n = ((j1 - 1 + pt_off) >> page_bits) - e0 + 1;
       if (n <= kPtCap) {
         for (int32_t e = tix(); e < n; e += (int32_t)blockDim.x) lds[e] = pt[e0 + e];
         staged = true;
@@ -399,7 +421,7 @@ __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L,
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
     const int32_t t = i * BS + tix();
-    if (t < k) em.out[t] = v[i];
+    if (t < k) em.put(t, t < L ? t : -1, v[i]);
   }
 }
 
@@ -419,7 +441,7 @@ __device__ __forceinline__ void write_stage_with(const Emit<kPaged>& em, const i
       const int32_t j = stage[t];
       const bool ok = (uint32_t)j < (uint32_t)L;  // a valid window position
       const int32_t v = value(ok ? j : 0);
-      em.out[t] = ok ? v : -1;
+      em.put(t, ok ? j : -1, ok ? v : -1);
     }
   }
 }
@@ -699,12 +721,12 @@ template <bool kPaged, int BS>
 __device__ __forceinline__ void load_table(const Emit<kPaged>& em, int32_t L,
                                            int32_t (&v)[table_per_thread<BS>()]) {
   if constexpr (kPaged) {
-    const int32_t n = L > 0 ? ((L - 1) >> em.page_bits) + 1 : 0;
-    if (n <= kPtCap) {
+    const int2 sp = em.table_span(L);
+    if (sp.y <= kPtCap) {
 #pragma unroll
       for (int q = 0; q < table_per_thread<BS>(); ++q) {
         const int32_t e = q * BS + tix();
-        v[q] = e < n ? em.pt[e] : 0;
+        v[q] = e < sp.y ? em.pt[sp.x + e] : 0;
       }
     }
   }
@@ -714,15 +736,15 @@ template <bool kPaged, int BS>
 __device__ __forceinline__ void store_table(Emit<kPaged>& em, int32_t* lds, int32_t L,
                                             const int32_t (&v)[table_per_thread<BS>()]) {
   if constexpr (kPaged) {
-    const int32_t n = L > 0 ? ((L - 1) >> em.page_bits) + 1 : 0;
-    if (n <= kPtCap) {
+    const int2 sp = em.table_span(L);
+    if (sp.y <= kPtCap) {
 #pragma unroll
       for (int q = 0; q < table_per_thread<BS>(); ++q) {
         const int32_t e = q * BS + tix();
-        if (e < n) lds[e] = v[q];
+        if (e < sp.y) lds[e] = v[q];
       }
       em.staged = true;
-      em.pt_first = 0;
+      em.pt_first = sp.x;
     }
   }
 }
@@ -1215,11 +1237,16 @@ template <bool kPaged>
 __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b) {
   Emit<kPaged> em;
   em.out = p.out + b * p.k;
+  em.out_raw = nullptr;
   em.page_bits = p.page_bits;
   em.staged = false;
   em.pt_first = 0;
+  em.pt_off = 0;
   if constexpr (kPaged) {
-    em.pt = p.page_table + b * p.pt_stride;
+    const int64_t tr = p.table_rows ? p.table_rows[b] : b;
+    em.pt = p.page_table + tr * p.pt_stride;
+    em.pt_off = p.table_starts ? p.table_starts[b] : 0;
+    if (p.out_raw) em.out_raw = p.out_raw + b * p.k;
     em.offset = 0;
   } else {
     em.pt = nullptr;
@@ -1796,7 +1823,7 @@ __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b,
     for (uint32_t i = t; i < total; i += kBlock) {
       const int32_t j = stage[i];
       const bool ok = ((uint32_t)j < (uint32_t)r.L) & (base + i < k);
-      if (ok) em.out[base + i] = value(j);
+      if (ok) em.put(base + i, j, value(j));
     }
   };
   if (kPaged && em.staged)
@@ -2066,6 +2093,17 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
                   const int32_t* row_starts, const int32_t* page_table,
                   int64_t page_table_stride, int32_t page_size, int32_t num_rows, int32_t k,
                   void* plan, size_t plan_bytes, int32_t* out, void* stream) {
+  return dsatopk_paged_packed(scores, score_stride, seq_lens, row_starts, page_table,
+                              page_table_stride, page_size, nullptr, nullptr, num_rows, k, plan,
+                              plan_bytes, out, nullptr, stream);
+}
+
+int dsatopk_paged_packed(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                         const int32_t* row_starts, const int32_t* page_table,
+                         int64_t page_table_stride, int32_t page_size,
+                         const int32_t* table_rows, const int32_t* table_starts,
+                         int32_t num_rows, int32_t k, void* plan, size_t plan_bytes,
+                         int32_t* out, int32_t* out_raw, void* stream) {
   int st = check_common(scores, score_stride, seq_lens, num_rows, k, out, plan, plan_bytes);
   if (st != DSATOPK_OK || num_rows == 0) return st;
   if (!page_table || page_table_stride < 1 || !is_pow2(page_size) || page_size > (1 << 20))
@@ -2083,6 +2121,9 @@ int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_
   p.k = k;
   p.out = out;
   p.plan = (int32_t*)plan;
+  p.table_rows = table_rows;
+  p.table_starts = table_starts;
+  p.out_raw = out_raw;
   return launch_rows<true>(p, (hipStream_t)stream);
 }
 

@@ -56,6 +56,15 @@ def paged(lib, **kw):
                              a["stream"])
 
 
+def paged_packed(lib, **kw):
+    a = dict(scores=A16, stride=64, lens=A16, starts=None, pt=A16, pts=8, ps=64, rows=A16,
+             tstarts=None, n=4, k=16, plan=None, plan_bytes=0, out=A16, raw=A16, stream=None)
+    a.update(kw)
+    return lib.dsatopk_paged_packed(a["scores"], a["stride"], a["lens"], a["starts"], a["pt"],
+                                    a["pts"], a["ps"], a["rows"], a["tstarts"], a["n"], a["k"],
+                                    a["plan"], a["plan_bytes"], a["out"], a["raw"], a["stream"])
+
+
 def ragged(lib, **kw):
     a = dict(scores=A16, stride=64, lens=A16, starts=None, offs=A16, rows=4, k=16, plan=None,
              plan_bytes=0, out=A16, stream=None)
@@ -77,6 +86,14 @@ def test_paged_rejects(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(k=0), 1), (dict(n=-1), 1), (dict(scores=None), 1), (dict(pt=None), 1),
+    (dict(ps=48), 1), (dict(scores=A4), 2), (dict(plan=A16, plan_bytes=1), 3),
+])
+def test_paged_packed_rejects(lib, kw, code):
+    assert paged_packed(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
     (dict(k=0), 1), (dict(k=4096), 1), (dict(offs=None), 1), (dict(scores=A4 + 8), 2),
     (dict(stride=6), 2), (dict(plan=A16, plan_bytes=8), 3),
 ])
@@ -88,6 +105,7 @@ def test_zero_rows_is_a_noop(lib):
     # nothing is launched and no pointer is looked at
     assert paged(lib, rows=0, scores=None, lens=None, out=None, pt=None) == 0
     assert ragged(lib, rows=0, scores=None, lens=None, out=None, offs=None) == 0
+    assert paged_packed(lib, n=0, scores=None, lens=None, out=None, pt=None, raw=None) == 0
     assert lib.dsatopk_plan(None, None, 0, 16, None, 0, None) == 0
 
 

@@ -306,3 +306,76 @@ def test_sustained_launch_sampled_rows(orc, name):
     words = _plan_words(plan)
     assert words[14] == 0, "a segment timed out waiting for its row"
     assert (words[12] == n) == (n <= SPLIT_CAP)
+
+
+PACKED = [
+    # (id, query rows per request, KV columns per request, k, largest window shift)
+    ("mixed_classes", [5, 2, 9], 20000, 2048, 999),
+    ("pages_layout", [3, 1, 4], 12000, 1000, 0),
+    ("long_rows", [3, 2], 131072 - 1024, 2048, 1000),
+]
+
+
+def _check_raw_pairs(out, raw, p, table_rows, table_starts):
+    """Slot for slot, out is raw mapped through the row's table row from
+    its table start; padding is -1 in both."""
+    k, ps = p.k, p.page_size
+    n = np.minimum(np.maximum(p.seq_lens, 0), k)
+    for b in range(p.num_rows):
+        j = raw[b, :n[b]].astype(np.int64)
+        q = j + (0 if table_starts is None else int(table_starts[b]))
+        t = b if table_rows is None else int(table_rows[b])
+        want = p.page_table[t, q // ps].astype(np.int64) * ps + q % ps
+        assert np.array_equal(out[b, :n[b]], want), b
+        assert (out[b, n[b]:] == -1).all() and (raw[b, n[b]:] == -1).all(), b
+
+
+@pytest.mark.parametrize("use_plan", [False, True])
+@pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
+def test_packed_paged_with_raw_positions(orc, case, use_plan):
+    """Packed rows (several query rows share a request's table row; table
+    starts shift the lookup) with the raw positions written in the same
+    launch, against the oracle's packed emit and its selection."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    cid, q_lens, kv, k, shift = case
+    p, tr, ts = workloads.packed_paged(4000 + len(cid), q_lens, kv, k, shift)
+    print(f"[gpu] packed {cid} rows={p.num_rows} plan={use_plan}", flush=True)
+    d = gpu_run.to_dev(p)
+    dev = d["scores"].device
+    plan = dt.plan(d["lens"], k, row_starts=d["starts"]) if use_plan else None
+    out, raw = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, k, row_starts=d["starts"],
+                        plan=plan, table_rows=torch.from_numpy(tr).to(dev),
+                        table_starts=torch.from_numpy(ts).to(dev), out_raw=True)
+    torch.cuda.synchronize()
+    out, raw = out.cpu().numpy(), raw.cpu().numpy()
+    want = orc.paged_packed(p.scores, p.seq_lens, p.row_starts, p.page_table, p.page_size, k,
+                            table_rows=tr, table_starts=ts)
+    assert_rows_equal(canonical(out, p.seq_lens, k), want, cid)
+    sel = orc.select(p.scores, p.seq_lens, p.row_starts, k)
+    assert_rows_equal(canonical(raw, p.seq_lens, k), sel, cid + " raw")
+    _check_raw_pairs(out, raw, p, tr, ts)
+
+
+@pytest.mark.parametrize("name", ["paged_small", "paged_decode", "paged_long", "paged_mixed"])
+def test_raw_positions_beside_paged(orc, name):
+    """The raw-position output on the plain PAGED workloads (with a plan):
+    the same selection, slot for slot with the paged values."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload(name)
+    print(f"[gpu] raw {name}", flush=True)
+    d = gpu_run.to_dev(p)
+    plan = dt.plan(d["lens"], p.k, row_starts=d["starts"])
+    out, raw = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, row_starts=d["starts"],
+                        plan=plan, out_raw=True)
+    torch.cuda.synchronize()
+    out, raw = out.cpu().numpy(), raw.cpu().numpy()
+    assert_rows_equal(canonical(out, p.seq_lens, p.k), expected(orc, p), name)
+    sel = orc.select(p.scores, p.seq_lens, p.row_starts, p.k)
+    assert_rows_equal(canonical(raw, p.seq_lens, p.k), sel, name + " raw")
+    _check_raw_pairs(out, raw, p, None, None)

@@ -27,6 +27,7 @@ from .configs import (  # noqa: F401
     WORKLOADS,
     Problem,
     make_workload,
+    packed_paged,
     scaled_decode,
     scaled_long,
     scaled_paged,

@@ -224,3 +224,35 @@ def all_trivial(seed: Optional[int] = None) -> Problem:
     scores = _normal(rng, (R, 8192))
     pt = random_page_tables(rng, R, 128, 4096)
     return Problem("all_trivial", "paged", 2048, scores, seq_lens, page_table=pt)
+
+
+def packed_paged(seed: int, q_lens, kv_len: int, k: int, max_shift: int = 0,
+                 page_size: int = PAGE_SIZE):
+    """Packed PAGED rows (the pages' packed layout): request r owns KV
+    columns [r * kv_len, (r + 1) * kv_len) of a batch-wide score axis and one
+    page-table row; its q_lens[r] query rows each select inside that span.
+    Row b of request r starts its window shift_b columns into the request
+    (shift_b uniform in [0, max_shift]): row_start = r * kv_len + shift_b and
+    table start shift_b. seq_len uniform in [k + 1, kv_len - shift_b]. N(0,1)
+    scores inside each window, 1e3 outside.
+
+    Returns (problem, table_rows, table_starts); the problem's page table has
+    one row per request."""
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens)
+    batch = len(q_lens)
+    table_rows = np.repeat(np.arange(batch), q_lens).astype(np.int32)
+    R = len(table_rows)
+    shifts = rng.integers(0, max_shift + 1, size=R).astype(np.int32)
+    seq_lens = rng.integers(k + 1, kv_len - shifts + 1).astype(np.int32)
+    row_starts = (table_rows.astype(np.int64) * kv_len + shifts).astype(np.int32)
+    stride = (batch * kv_len + 3) // 4 * 4
+    scores = np.full((R, stride), OUTSIDE_SCORE, dtype=np.float32)
+    for b in range(R):
+        s, L = int(row_starts[b]), int(seq_lens[b])
+        scores[b, s:s + L] = rng.standard_normal(L, dtype=np.float32)
+    width = -(-kv_len // page_size)
+    pt = random_page_tables(rng, batch, width, max(width, 4096))
+    p = Problem(f"packed_paged_{batch}x{kv_len}", "paged", k, scores, seq_lens,
+                row_starts=row_starts, page_table=pt, page_size=page_size)
+    return p, table_rows, shifts
