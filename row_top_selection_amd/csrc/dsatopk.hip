@@ -421,27 +421,49 @@ __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L,
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
     const int32_t t = i * BS + tix();
-    if (t < k) em.put(t, t < L ? t : -1, v[i]);
+    if (t < k) em.out[t] = v[i];
+  }
+  if (kPaged && em.out_raw) {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int32_t t = i * BS + tix();
+      if (t < k) em.out_raw[t] = t < L ? t : -1;
+    }
   }
 }
 
 // Final coalesced store of the k staged positions. A position outside
 // [0, L) cannot come out of a correct cut; it is written as -1 rather than
 // used to index the page table.
-// Fully unrolled (k <= kMaxK) with unconditional loads, so the stage and
-// page-table lookups of all iterations are in flight together.
+// Fully unrolled (k <= kMaxK) in three straight-line phases: every stage
+// read (the stage holds at least kMaxK words, so slots past k are read but
+// not used), then every page-table lookup, then the stores. All reads of a
+// phase are in flight together, not one dependent pair per slot.
 template <bool kPaged, int BS, class V>
 __device__ __forceinline__ void write_stage_with(const Emit<kPaged>& em, const int32_t* stage,
                                                  int32_t L, int32_t k, V value) {
   static_assert(kMaxK % BS == 0, "whole iterations");
+  constexpr int kIter = kMaxK / BS;
+  int32_t j[kIter];
+  int32_t v[kIter];
 #pragma unroll
-  for (int i = 0; i < kMaxK / BS; ++i) {
+  for (int i = 0; i < kIter; ++i) j[i] = stage[i * BS + tix()];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const bool ok = (uint32_t)j[i] < (uint32_t)L;  // a valid window position
+    j[i] = ok ? j[i] : -1;
+    v[i] = value(ok ? j[i] : 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
     const int32_t t = i * BS + tix();
-    if (t < k) {
-      const int32_t j = stage[t];
-      const bool ok = (uint32_t)j < (uint32_t)L;  // a valid window position
-      const int32_t v = value(ok ? j : 0);
-      em.put(t, ok ? j : -1, ok ? v : -1);
+    if (t < k) em.out[t] = j[i] >= 0 ? v[i] : -1;
+  }
+  if (kPaged && em.out_raw) {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int32_t t = i * BS + tix();
+      if (t < k) em.out_raw[t] = j[i];
     }
   }
 }
