@@ -1572,74 +1572,121 @@ __device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* 
 }
 
 // The exact cut among n (key, position) pairs in LDS, all inside one
-// level-1 bin, taking `need` of them: key digits 19..12, 11..4, 3..0 and,
-// for ties at the k-th key, position digits 16..9, 8..1, 0. One wave, no
-// workgroup barriers; h2 / h3 / h4 are scratch histograms. Returns
-// (tau, pos): select key > tau, or key == tau and position <= pos.
-__device__ __forceinline__ uint64_t resolve_pairs_wave(const uint2* cand, uint32_t n,
-                                                       uint32_t prefix, uint32_t need,
-                                                       SmemSplit& sm) {
-  const int lane = lane_id();
-  uint32_t pbits = 12;  // key bits fixed so far (from the top)
-  const uint32_t key_shift[3] = {12, 4, 0};
-  const uint32_t key_width[3] = {8, 8, 4};
-  uint32_t* hs[3] = {sm.h2, sm.h3, sm.h4};
-  uint32_t tau = 0;
-  bool resolved = false;
-  uint32_t shift_done = 20;
-  for (int d = 0; d < 3; ++d) {
-    const uint32_t sh = key_shift[d];
-    const uint32_t wd = key_width[d];
-    uint32_t* h = hs[d];
-    for (uint32_t i = lane; i < (1u << wd); i += 64) h[i] = 0;
-    wave_lds_sync();
-    const uint32_t hi_shift = sh + wd;
-    for (uint32_t i = lane; i < n; i += 64) {
-      const uint32_t kk = cand[i].x;
-      if ((kk >> hi_shift) == prefix) lds_inc(&h[(kk >> sh) & ((1u << wd) - 1u)]);
-    }
-    wave_lds_sync();
-    const BinHit b = wd == 8 ? wave_find<256, true>(h, need) : wave_find<16, true>(h, need);
-    need -= b.before;
-    prefix = (prefix << wd) | b.bin;
-    pbits += wd;
-    shift_done = sh;
-    if (b.cnt == need) {
-      resolved = true;
-      break;
-    }
+// level-1 bin, taking `need` of them; the whole workgroup. The keys' AND
+// and OR give the bits in which they differ: 8-bit digit rounds run over
+// those bits only (the bits below them are the same in every key), each a
+// histogram of the candidates still matching the digits fixed so far.
+// Ties at the k-th key take the lowest positions: a tie class of at most 64
+// elements is gathered and ranked on lane masks, a larger one takes
+// position digits (8, 8 and 1 bits). Returns (tau, pos) packed as the
+// round result: select key > tau, or key == tau + 1 and position <= pos
+// (pos = kPackAllPos: every such key).
+__device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint32_t n,
+                                                        uint32_t need, SmemSplit& sm) {
+  const int32_t t = tix();
+  uint32_t a = 0xffffffffu, o = 0u;
+  for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+    const uint32_t kk = cand[i].x;
+    a &= kk;
+    o |= kk;
   }
-  if (resolved) {
-    // every element of the final bin is taken: its lowest key is the cut,
-    // with all ties at it taken
-    const uint32_t lo = prefix << shift_done;
-    tau = lo ? lo - 1u : 0u;  // select key > lo - 1, i.e. key >= lo
-    return ((uint64_t)kPackAllPos << 32) | tau;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a &= (uint32_t)__shfl_xor((int)a, d);
+    o |= (uint32_t)__shfl_xor((int)o, d);
   }
-  tau = prefix;  // all 32 key bits
-  // ties: the need lowest positions among key == tau
-  uint32_t pprefix = 0;
-  const uint32_t pos_shift[3] = {9, 1, 0};
-  const uint32_t pos_width[3] = {8, 8, 1};
-  for (int d = 0; d < 3; ++d) {
-    const uint32_t sh = pos_shift[d];
-    const uint32_t wd = pos_width[d];
-    uint32_t* h = hs[d];
-    wave_lds_sync();
-    for (uint32_t i = lane; i < (1u << wd); i += 64) h[i] = 0;
-    wave_lds_sync();
-    const uint32_t hi_shift = sh + wd;
-    for (uint32_t i = lane; i < n; i += 64) {
+  if (t == 0) {
+    sm.bcast[0] = 0xffffffffu;
+    sm.bcast[1] = 0u;
+    sm.tie_n = 0u;
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    atomicAnd(&sm.bcast[0], a);
+    atomicOr(&sm.bcast[1], o);
+  }
+  __syncthreads();
+  const uint32_t all_and = __builtin_amdgcn_readfirstlane(sm.bcast[0]);
+  const uint32_t diff = all_and ^ __builtin_amdgcn_readfirstlane(sm.bcast[1]);
+  __syncthreads();  // the searches below broadcast through bcast
+  uint32_t fixed = all_and & ~diff;  // the key bits decided so far
+  uint32_t cnt = n;
+  if (diff) {
+    const int lo_bit = __builtin_ctz(diff);
+    for (int top = 31 - __builtin_clz(diff); top >= lo_bit; top -= 8) {
+      const int width = top - lo_bit + 1 < 8 ? top - lo_bit + 1 : 8;
+      const int sh = top - width + 1;
+      const uint32_t above = top == 31 ? 0u : fixed >> (top + 1);
+      sm.h2[t] = 0u;
+      __syncthreads();
+      for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+        const uint32_t kk = cand[i].x;
+        if (top == 31 || (kk >> (top + 1)) == above)
+          lds_inc(&sm.h2[(kk >> sh) & ((1u << width) - 1u)]);
+      }
+      __syncthreads();
+      const BinHit b = wave0_find<256, true>(sm.h2, need, sm);
+      need -= b.before;
+      fixed |= b.bin << sh;
+      cnt = b.cnt;
+      if (b.cnt == need) {
+        // every key of this digit bin is taken: the cut is its lowest key
+        // (key >= lo; lo = 0 leaves out only the columns outside the window)
+        const uint32_t lo = (fixed >> sh) << sh;
+        return ((uint64_t)kPackAllPos << 32) | (lo ? lo - 1u : 0u);
+      }
+    }
+  } else if (cnt == need) {
+    return ((uint64_t)kPackAllPos << 32) | (fixed ? fixed - 1u : 0u);
+  }
+  const uint32_t tau = fixed;  // every key bit decided: the tied key
+  if (cnt <= 64u) {
+    for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
       const uint2 e = cand[i];
-      if ((e.x == tau) & ((e.y >> hi_shift) == pprefix))
-        lds_inc(&h[(e.y >> sh) & ((1u << wd) - 1u)]);
+      if (e.x == tau) {
+        const uint32_t slot = atomicAdd(&sm.tie_n, 1u);
+        if (slot < 64u) sm.h3[slot] = e.y;
+      }
     }
-    wave_lds_sync();
-    const BinHit b = wd == 8 ? wave_find<256, false>(h, need) : wave_find<2, false>(h, need);
+    __syncthreads();
+    const int lane = lane_id();
+    const uint32_t p = lane < (int)cnt ? sm.h3[lane] : 0u;
+    uint64_t live = cnt >= 64u ? ~0ull : (1ull << cnt) - 1ull;
+#pragma unroll
+    for (int b = 16; b >= 0; --b) {
+      const uint64_t zeros = __ballot(((p >> b) & 1u) == 0u) & live;
+      const uint32_t c0 = (uint32_t)__builtin_popcountll(zeros);
+      if (need <= c0) {
+        live = zeros;
+      } else {
+        need -= c0;
+        live &= ~zeros;
+      }
+    }
+    const uint32_t pos = read_lane(p, live ? __builtin_ctzll(live) : 0);
+    __syncthreads();  // h3 and tie_n may be reused by the caller
+    return ((uint64_t)pos << 32) | (tau - 1u);
+  }
+  // a large tie class: position digits 16..9, 8..1, 0
+  uint32_t pprefix = 0;
+  const int pos_shift[3] = {9, 1, 0};
+  const int pos_width[3] = {8, 8, 1};
+  for (int d = 0; d < 3; ++d) {
+    const int sh = pos_shift[d];
+    const int wd = pos_width[d];
+    sm.h2[t] = 0u;
+    __syncthreads();
+    for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+      const uint2 e = cand[i];
+      if ((e.x == tau) & ((e.y >> (sh + wd)) == pprefix))
+        lds_inc(&sm.h2[(e.y >> sh) & ((1u << wd) - 1u)]);
+    }
+    __syncthreads();
+    const BinHit b = wave0_find<256, false>(sm.h2, need, sm);
     need -= b.before;
     pprefix = (pprefix << wd) | b.bin;
   }
-  return ((uint64_t)pprefix << 32) | (tau - 1u);  // key > tau - 1 and pos cut
+  return ((uint64_t)pprefix << 32) | (tau - 1u);
 }
 
 // One segment of a split row: the segment sits in registers like a short
@@ -1736,11 +1783,7 @@ __device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b,
         lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
       }
       __syncthreads();
-      if (w == 0) res = resolve_pairs_wave(lcand, h.cnt, h.bin, need, sm);
-      if (t == 0) s_word[0] = (uint32_t)res, s_word[1] = (uint32_t)(res >> 32);
-      __syncthreads();
-      res = ((uint64_t)s_word[1] << 32) | s_word[0];
-      __syncthreads();
+      res = resolve_pairs_group(lcand, h.cnt, need, sm);
       sy.publish(round, res);
     }
     res = sy.result(round, last, res);
