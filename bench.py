@@ -16,8 +16,12 @@ Also reported (same JSON line):
                 lengths) over its mean launch time from HIP events around a
                 graph of back-to-back launches.
   sustained     the same per-row shapes with enough rows for >= 1 GiB of
-                scores per launch (paged_decode x32768, paged_long x2048).
-  workloads     every named workload, one launch per iteration, cold.
+                scores per launch (L = 8192 ... 131072), timed in steady
+                state: after 0.1 s of untimed replays (the GPU's clocks ramp
+                up over the first ~10 ms of continuous work), the mean of 5
+                replays of 20 launches.
+  workloads     every named workload, one launch per iteration, cold, after
+                the same 0.1 s of untimed replays.
   cpu_baseline  the oracle on this host's cores over a bounded sample.
 """
 from __future__ import annotations
@@ -37,6 +41,7 @@ if ROOT not in sys.path:
 METRIC = "DSA top-k rows/s + achieved HBM GB/s (paged decode, L=8K–128K, k=2048)"
 HBM_PEAK_GBPS = 8000.0
 ROTATION_BYTES = 1 << 30
+SETTLE_S = 0.1  # untimed replays before a sustained measurement
 COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_rows_wide_kernel_paged_decode.md")
 
@@ -190,11 +195,16 @@ def time_graph_steps(fn, steps: int, warmup: int) -> float:
     return time.perf_counter() - t0
 
 
-def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
+def kernel_time_us(fn, iters: int, warmup: int = 3, settle_s: float = 0.0,
+                   reps: int = 1) -> float:
     """Mean duration of fn(i)'s launches: `iters` calls captured back to back
-    in one HIP graph, replayed between two HIP events recorded on the stream
-    the graph runs on (torch's current stream), divided by `iters`. The graph
-    keeps host launch overhead out of short launches."""
+    in one HIP graph, replayed `reps` times between two HIP events recorded on
+    the stream the graph runs on (torch's current stream), divided by
+    iters * reps. The graph keeps host launch overhead out of short launches.
+    With settle_s, untimed replays run for that long first: the GPU raises
+    its clocks over the first ~10 ms of continuous work (the first replay
+    after an idle spell runs about a tenth slower), so a steady rate is only
+    seen after it."""
     import torch
 
     for i in range(warmup):
@@ -202,13 +212,18 @@ def kernel_time_us(fn, iters: int, warmup: int = 3) -> float:
     g = capture_steps(fn, warmup, iters)
     g.replay()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    g.replay()
+    for _ in range(reps):
+        g.replay()
     b.record()
     torch.cuda.synchronize()
-    return 1e3 * a.elapsed_time(b) / iters
+    return 1e3 * a.elapsed_time(b) / (iters * reps)
 
 
 def cpu_baseline(p, budget_s: float = 12.0) -> dict:
@@ -316,9 +331,9 @@ def only_workload(name: str):
     return workloads.make_workload(name)
 
 
-def measure_workload(p, iters: int, **packed) -> dict:
+def measure_workload(p, iters: int, settle_s: float = SETTLE_S, reps: int = 1, **packed) -> dict:
     r = Runner(p, **packed)
-    us = kernel_time_us(r.transform, iters)
+    us = kernel_time_us(r.transform, iters, settle_s=settle_s, reps=reps)
     b = algorithmic_bytes(p)
     if packed.get("raw"):
         b = dict(b, raw=b["out"], total=b["total"] + b["out"])
@@ -416,8 +431,10 @@ def main(argv=None):
         # launch (the decode and long-context shapes, and three between)
         sus = {}
         for name, mk in SUSTAINED.items():
-            res = measure_workload(mk(workloads), 20)
+            # steady state: 0.1 s of untimed replays, then 5 x 20 launches
+            res = measure_workload(mk(workloads), 20, reps=5)
             res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
+            res["timing"] = f"mean of 5 replays of 20 launches after {SETTLE_S} s of replays"
             sus[name] = res
             torch.cuda.empty_cache()
         line["sustained"] = sus
@@ -434,7 +451,7 @@ def main(argv=None):
         line["packed"] = {
             "packed_extend": measure_workload(pk, 20, table_rows=tr, table_starts=ts, raw=True),
             "paged_decode_x32768_raw": measure_workload(workloads.scaled_decode(32768), 20,
-                                                        raw=True),
+                                                        reps=5, raw=True),
         }
         torch.cuda.empty_cache()
     line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)

@@ -314,9 +314,13 @@ struct RegSrc {
   __device__ __forceinline__ void for_each(F&& f) const {
     int32_t base = tix() * 4 + origin;
     asm volatile("" : "+v"(base));
+    // the slice bound as an opaque scalar: every slice test is one scalar
+    // compare, not a lane mask rebuilt in VGPRs for each pass
+    int32_t il = ilast;
+    asm volatile("" : "+s"(il));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      if (i <= ilast) {
+      if (i <= il) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) f(key[i][c], base + i * BS * 4 + c);
       }
