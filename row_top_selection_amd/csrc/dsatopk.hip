@@ -1200,8 +1200,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         key[q] = edge ? key_at(x, a0 + q, rv) : order_key(x);
         sel[q] = key[q] >= Tc;
       }
-      append4(key, sel, a0, d);  // c0 is a multiple of 4: c % 4 == d
+      // the chunk is in registers as keys: its buffer refills before the
+      // append's barrier, not after it
       issue(buf[d], c + kS1Depth);
+      append4(key, sel, a0, d);  // c0 is a multiple of 4: c % 4 == d
     }
   }
   __syncthreads();  // every wave's last pairs are in the list
@@ -1212,6 +1214,24 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // then all above the cut, where their order does not matter); on the keys
   // themselves otherwise.
   const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
+  // The row's page-table entries, when at most kBins - kMaxK, into registers
+  // now (their loads overlap the cut), and into the histogram's upper part
+  // once the cut is found: the stage below it takes at most kMaxK words.
+  // The emit then looks them up in LDS instead of waiting on global loads.
+  constexpr int kTabCap = kBins - kMaxK;
+  constexpr int kTabPer = kTabCap / BS;
+  static_assert(kTabCap % BS == 0, "whole table entries per thread");
+  const int32_t L = rv.span - rv.rem;
+  const int2 tsp = em.table_span(L);
+  const bool tab = kPaged && tsp.y <= kTabCap;
+  int32_t tv[kTabPer];
+  if (tab) {
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) {
+      const int32_t e = q * BS + tix();
+      tv[q] = e < tsp.y ? em.pt[tsp.x + e] : 0;
+    }
+  }
   {
     uint32_t sat = 0;
     for (uint32_t i = (uint32_t)tix(); i < n; i += BS)
@@ -1238,6 +1258,19 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   }
   __syncthreads();
   const Cut cut = refine_in_registers<BS>(src, sm, kk, offsets);
+  // every search of the cut ended with a barrier after its last histogram
+  // read; the tie ranking reads only the first 64 words
+  int32_t* table = stage + kMaxK;
+  Emit<kPaged> et = em;
+  if (tab) {
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) {
+      const int32_t e = q * BS + tix();
+      if (e < tsp.y) table[e] = tv[q];
+    }
+    et.staged = true;
+    et.pt_first = tsp.x;
+  }
   if (cut.pos == kAllPos) {
     const uint32_t lo = cut.prefix << cut.shift;
     const uint32_t thr = lo ? lo : 1u;
@@ -1255,7 +1288,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   }
   for (int32_t i = (int32_t)kk + tix(); i < k; i += BS) stage[i] = -1;
   __syncthreads();
-  write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
+  write_stage<kPaged, BS>(et, stage, L, k, table);
   return true;
 }
 
