@@ -173,10 +173,14 @@ struct Emit {
     if constexpr (kPaged) {
       // an LDS pointer by type, so that the read is an LDS read even where
       // the compiler merges this path with the global one
-      const __attribute__((address_space(3))) int32_t* e =
-          (const __attribute__((address_space(3))) int32_t*)lds;
-      const int32_t q = j + pt_off;
-      return map(q, e[(q >> page_bits) - pt_first]);
+      // entry q >> page_bits sits at lds[(q >> page_bits) - pt_first]: its
+      // LDS byte address is one shift-add onto a scalar base
+      using lds_i32 = const __attribute__((address_space(3))) int32_t;
+      const uint32_t base =
+          (uint32_t)(uintptr_t)(lds_i32*)lds - (uint32_t)pt_first * 4u;
+      const uint32_t q = (uint32_t)(j + pt_off);
+      lds_i32* e = (lds_i32*)(uintptr_t)(((q >> page_bits) << 2) + base);
+      return map((int32_t)q, *e);
     } else {
       return j + offset;
     }
@@ -412,26 +416,54 @@ struct ListSrc {
   }
 };
 
+// A raw buffer over the n int32 words at p. Stores through it take their
+// address from one VGPR offset (plus the instruction's immediate offset),
+// and the hardware drops a store whose offset is at or past n words, so the
+// slots past k need no lane compare.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t words_buffer(int32_t* p, int32_t n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(n * 4),
+                                           0x00020000);
+}
+
+// Cache policy of the output stores: non-temporal, like the score loads
+// (the outputs are not read back by this library). On MI355X this takes
+// 2-4% off the short, big-register and streaming kernels' launches; the
+// mid kernel's 16 float4 x 256-thread rows ran 5% slower with it, so that
+// configuration stores with the default policy.
+constexpr int kStreamingStore = 2;
+constexpr int kDefaultStore = 0;
+
+// Slot i * BS + t of a row's output (t = this thread's index): the slot's
+// byte offset is in the VGPR offset, where the range check sees it.
+template <int BS, int kPolicy = kStreamingStore>
+__device__ __forceinline__ void store_slot(__amdgpu_buffer_rsrc_t r, int32_t t, int i, int32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (t + i * BS) * 4, 0, kPolicy);
+}
+
 template <bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L, int32_t k) {
   // all table loads before any store: one memory round trip, not one per slot
   constexpr int kIter = kMaxK / BS;
+  const int32_t t = tix();
   int32_t v[kIter];
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
-    const int32_t t = i * BS + tix();
-    v[i] = t < L ? em.value(t) : -1;
+    const int32_t s = i * BS + t;
+    v[i] = s < L ? em.value(s) : -1;
   }
+  const __amdgpu_buffer_rsrc_t ro = words_buffer(em.out, k);
 #pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int32_t t = i * BS + tix();
-    if (t < k) em.out[t] = v[i];
-  }
+  for (int i = 0; i < kIter; ++i) store_slot<BS>(ro, t, i, v[i]);
   if (kPaged && em.out_raw) {
+    const __amdgpu_buffer_rsrc_t rr = words_buffer(em.out_raw, k);
 #pragma unroll
     for (int i = 0; i < kIter; ++i) {
-      const int32_t t = i * BS + tix();
-      if (t < k) em.out_raw[t] = t < L ? t : -1;
+      const int32_t s = i * BS + t;
+      store_slot<BS>(rr, t, i, s < L ? s : -1);
     }
   }
 }
@@ -443,45 +475,46 @@ __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L,
 // read (the stage holds at least kMaxK words, so slots past k are read but
 // not used), then every page-table lookup, then the stores. All reads of a
 // phase are in flight together, not one dependent pair per slot.
-template <bool kPaged, int BS, class V>
+template <bool kPaged, int BS, int kPolicy, class V>
 __device__ __forceinline__ void write_stage_with(const Emit<kPaged>& em, const int32_t* stage,
                                                  int32_t L, int32_t k, V value) {
   static_assert(kMaxK % BS == 0, "whole iterations");
   constexpr int kIter = kMaxK / BS;
+  // one thread index for every phase: the stage reads and the stores take
+  // their slot from an immediate offset
+  const int32_t t = tix();
   int32_t j[kIter];
   int32_t v[kIter];
 #pragma unroll
-  for (int i = 0; i < kIter; ++i) j[i] = stage[i * BS + tix()];
+  for (int i = 0; i < kIter; ++i) j[i] = stage[i * BS + t];
 #pragma unroll
   for (int i = 0; i < kIter; ++i) {
     const bool ok = (uint32_t)j[i] < (uint32_t)L;  // a valid window position
+    const int32_t vv = value(ok ? j[i] : 0);
     j[i] = ok ? j[i] : -1;
-    v[i] = value(ok ? j[i] : 0);
+    v[i] = ok ? vv : -1;
   }
+  const __amdgpu_buffer_rsrc_t ro = words_buffer(em.out, k);
 #pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int32_t t = i * BS + tix();
-    if (t < k) em.out[t] = j[i] >= 0 ? v[i] : -1;
-  }
+  for (int i = 0; i < kIter; ++i) store_slot<BS, kPolicy>(ro, t, i, v[i]);
   if (kPaged && em.out_raw) {
+    const __amdgpu_buffer_rsrc_t rr = words_buffer(em.out_raw, k);
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int32_t t = i * BS + tix();
-      if (t < k) em.out_raw[t] = j[i];
-    }
+    for (int i = 0; i < kIter; ++i) store_slot<BS, kPolicy>(rr, t, i, j[i]);
   }
 }
 
 // The k staged positions, mapped, to the row's output. `lds_table` is the
 // workgroup's LDS copy of the page table, used when the emit staged it.
-template <bool kPaged, int BS = kBlock>
+template <bool kPaged, int BS = kBlock, int kPolicy = kStreamingStore>
 __device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_t* stage,
                                             int32_t L, int32_t k, const int32_t* lds_table) {
   if (kPaged && em.staged)
-    write_stage_with<kPaged, BS>(em, stage, L, k,
-                                 [&](int32_t j) { return em.value_lds(j, lds_table); });
+    write_stage_with<kPaged, BS, kPolicy>(em, stage, L, k,
+                                          [&](int32_t j) { return em.value_lds(j, lds_table); });
   else
-    write_stage_with<kPaged, BS>(em, stage, L, k, [&](int32_t j) { return em.value(j); });
+    write_stage_with<kPaged, BS, kPolicy>(em, stage, L, k,
+                                          [&](int32_t j) { return em.value(j); });
 }
 
 // A bin search whose result every thread needs: wave 0 searches and the
@@ -704,9 +737,10 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint3
 // about a fifth on MI355X.
 constexpr int kStreamingLoad = 2;
 
-// A raw buffer over the row's nvec aligned vectors: its loads take the
-// slice offset from a scalar register, and the hardware returns zeros for
-// vectors past the end instead of reading them, so no load needs a compare.
+// A raw buffer over the row's nvec aligned vectors: the hardware returns
+// zeros for vectors past the end instead of reading them, so no load needs a
+// compare. Every load puts its whole offset (thread and slice) in the VGPR
+// offset, which the range check covers; the scalar offset is left at 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const float4* base4, int32_t nvec) {
   const uint64_t a = reinterpret_cast<uint64_t>(base4);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -725,7 +759,7 @@ __device__ __forceinline__ void load_vectors(const float4* base4, int32_t nvec, 
   const int32_t off = (v0 + tix()) * 16;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    x[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, i * BS * 16,
+    x[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + i * BS * 16, 0,
                                                                             kStreamingLoad));
 }
 
@@ -884,7 +918,8 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
         (uint32_t)k, stage, sm);
   }
   __syncthreads();
-  write_stage<kPaged, BS>(em, stage, L, k, sm.pt);
+  write_stage<kPaged, BS, (NV == kLargeVec && BS == kBlock) ? kDefaultStore : kStreamingStore>(
+      em, stage, L, k, sm.pt);
 }
 
 template <int NV, bool kPaged, int BS = kBlock>
@@ -1047,7 +1082,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   uint32_t n = 0;
   float4 buf[kS1Depth];
   auto issue = [&](float4& b, int32_t c) {
-    b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, c * BS * 16,
+    b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + c * BS * 16, 0,
                                                                          kStreamingLoad));
   };
   // Chunk c's pairs (key[q], a0 + q - rem) with sel[q] to the list after
