@@ -446,18 +446,25 @@ __device__ __forceinline__ void store_slot(__amdgpu_buffer_rsrc_t r, int32_t t, 
 
 template <bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void write_trivial(const Emit<kPaged>& em, int32_t L, int32_t k) {
-  // all table loads before any store: one memory round trip, not one per slot
+  // all table loads before any store: one memory round trip, not one per
+  // slot. Every slot loads (a slot past the window looks up the window's
+  // last position, which is in bounds, and its value is replaced), so no
+  // load sits behind a branch and its own wait.
   constexpr int kIter = kMaxK / BS;
   const int32_t t = tix();
   int32_t v[kIter];
 #pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int32_t s = i * BS + t;
-    v[i] = s < L ? em.value(s) : -1;
+  for (int i = 0; i < kIter; ++i) v[i] = -1;
+  if (L > 0) {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int32_t s = i * BS + t;
+      v[i] = em.value(s < L ? s : L - 1);
+    }
   }
   const __amdgpu_buffer_rsrc_t ro = words_buffer(em.out, k);
 #pragma unroll
-  for (int i = 0; i < kIter; ++i) store_slot<BS>(ro, t, i, v[i]);
+  for (int i = 0; i < kIter; ++i) store_slot<BS>(ro, t, i, i * BS + t < L ? v[i] : -1);
   if (kPaged && em.out_raw) {
     const __amdgpu_buffer_rsrc_t rr = words_buffer(em.out_raw, k);
 #pragma unroll
@@ -988,16 +995,17 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
 
 // A long row in one pass over its scores. The workgroup streams the row
 // in chunks, kS1Depth chunks in flight, and keeps in LDS the (key,
-// position) pairs of every element with key >= T. T starts at 1 (every
-// window element; columns outside the window have key 0) and only rises:
-// when the list could not take another chunk, T becomes a key no higher
-// than the k-th largest of the list (its 24-bit prefix), and only the pairs
-// >= T stay. The k-th largest of a subset never exceeds the k-th largest of
-// the row, so every pair the row's top k needs is kept. After the last
-// chunk the pairs go to registers and the register path resolves the exact
-// cut (ties included) and emits. Returns false, having written nothing,
-// when ties keep the list too full to take another chunk; the caller then
-// runs the two-pass path.
+// position) pairs of every element with key >= T. T opens at a key found
+// from the row's first chunks (below) and only rises: when the list could
+// not take another chunk, T becomes a key no higher than the k-th largest
+// of the list (its 24-bit prefix), and only the pairs >= T stay. The k-th
+// largest of a subset never exceeds the k-th largest of the row, so once
+// at least k pairs reached T, every pair the row's top k needs is in the
+// list. After the last chunk the register path resolves the exact cut over
+// the list (ties included) and emits. Returns false, having written
+// nothing, when ties keep the list too full to take another chunk or when
+// fewer than k keys of the row reached T; the caller then runs the
+// two-pass path.
 // From per-wave counts cnt[0 .. W) (written before a barrier the caller
 // has passed): x = the count of the waves before this one, y = the total.
 template <int W>
@@ -1154,10 +1162,18 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
 
   // Warm start: the first kS1Depth chunks (16384 elements; a long span has
-  // more) are a register row. Their exact cut gives T (the k-th largest key
-  // of a subset, so no higher than the row's) and their k winners open the
-  // list, in place of the compactions a list starting from T = 1 needs to
-  // climb there.
+  // more) are a register row. T opens at the lowest key of the level-1 bin
+  // that holds the kt-th largest key of this subset, and every subset pair
+  // at or above it opens the list, with kt the count that, at the subset's
+  // rate, puts about 1.5 k keys of the whole span at or above the kt-th key
+  // (the rest of the bin adds a few hundred on N(0,1) rows). On rows whose large keys are spread along the
+  // span the list then never reaches the compaction mark (opening at the
+  // subset's k-th key, the list of a 131072-column row took about 4000
+  // appends and two compactions). A span where fewer than k keys reach T
+  // (its largest keys crowd its first columns) is found after the last
+  // chunk and re-read by the two-pass path. When the subset's pairs at or
+  // above T might not fit the list (a huge bin), the list opens with the
+  // subset's exact top k instead, T being its k-th key.
   {
     uint32_t wk[kS1Depth][4];
 #pragma unroll
@@ -1181,11 +1197,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
         for (int q = 0; q < 4; ++q) lds_add(&fin.hist[wk[d][q] >> 20], one);
     }
     __syncthreads();
-    // The level-1 bin of the subset's k-th largest key: its lowest key is a
-    // valid T, and the pairs at or above it (k plus the rest of that bin)
-    // open the list when they fit; else the exact cut of the subset, which
-    // opens it with exactly k.
-    const BinHit h = group_find<kBins, true, BS>(fin.hist, (uint32_t)k, fin);
+    constexpr int32_t kWarm = kS1Depth * kS1Chunk;
+    const uint32_t kt = (uint32_t)min(
+        k, max(1, (int32_t)((3 * k * kWarm + 2 * rv.span - 1) / (2 * rv.span))));
+    const BinHit h = group_find<kBins, true, BS>(fin.hist, kt, fin);
     uint32_t tau;
     if (h.before + h.cnt <= (uint32_t)(kS1Cap - kS1Chunk)) {
       // the search closed with a barrier: nothing reads the final-cut space
@@ -1242,7 +1257,9 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     }
   }
   __syncthreads();  // every wave's last pairs are in the list
-  if (overflow) return false;
+  // fewer than k pairs: T opened above the span's k-th key (or the window
+  // holds keys below every threshold, i.e. all-ones NaNs): two passes
+  if (overflow || n < (uint32_t)k) return false;
 
   // The cut and the stage run on the list where it stands. On offsets above
   // T when fewer than the kk taken pairs reach the offset bound (those are
@@ -1372,14 +1389,81 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32
   return r;
 }
 
-// row_info of the row a whole workgroup serves, in scalar registers.
-__device__ __forceinline__ RowInfo group_row_info(const Params& p, int64_t b) {
-  RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
+// Every word a row's workgroup reads before its scores, loaded together:
+// one memory round trip before the first score load instead of a chain of
+// dependent ones (under a full-chip load each round trip costs
+// microseconds). An optional array that is absent is read at a valid
+// stand-in address (the row's length) and its value replaced afterwards, so
+// no load waits on the test of another. The plan words are read only when
+// with_plan; a plan passed to a call is at least dsatopk_plan_bytes long
+// (checked on the host), so its row words are in bounds whatever it holds.
+struct RowMeta {
+  RowInfo r;
+  int32_t trow;    // PAGED: page-table row
+  int32_t tstart;  // PAGED: table position of window position 0
+  int32_t offset;  // RAGGED: the row's out offset
+  bool split;      // the plan sends the row to the split kernel
+};
+
+template <bool kPaged>
+__device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool with_plan) {
+  const int32_t* a_len = p.seq_lens + b;
+  const int32_t* a_rs = p.row_starts ? p.row_starts + b : a_len;
+  const int32_t* a_tr = (kPaged && p.table_rows) ? p.table_rows + b : a_len;
+  const int32_t* a_ts = (kPaged && p.table_starts) ? p.table_starts + b : a_len;
+  const int32_t* a_of = kPaged ? a_len : p.out_offsets + b;
+  const bool hp = with_plan && p.plan != nullptr;
+  const int32_t* a_pm = hp ? p.plan + kPlanWordMagic : a_len;
+  const int32_t* a_pr = hp ? p.plan + kPlanWordRows : a_len;
+  const int32_t* a_ps = hp ? p.plan + plan_nseg_word(p.num_rows) + b : a_len;
+  const int32_t* a_pl = hp ? p.plan + plan_slot_word(p.num_rows) + b : a_len;
+  int32_t len = *a_len, rs = *a_rs, tr = *a_tr, ts = *a_ts, of = *a_of;
+  int32_t pm = *a_pm, pr = *a_pr, ps = *a_ps, pl = *a_pl;
+  // every value is needed here: the compiler may not sink a load into the
+  // branch that uses it (which would put it behind another load's wait)
+  asm volatile("" : "+s"(len), "+s"(rs), "+s"(tr), "+s"(ts), "+s"(of), "+s"(pm), "+s"(pr),
+               "+s"(ps), "+s"(pl));
+  RowMeta m;
+  RowInfo& r = m.r;
+  r.L = len < 0 ? 0 : (len > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : len);
+  r.s = p.row_starts ? rs : 0;
+  r.span = r.L + (r.s & 3);
+  r.cls = (r.L <= p.k || r.span <= kSmallVec * 4 * kBlock) ? kClassShort
+          : (r.span <= kLargeVec * 4 * kBlock)              ? kClassMid
+          : (r.span <= kBigVec * 4 * kBigBlock)             ? kClassBig
+                                                            : kClassLong;
   r.L = __builtin_amdgcn_readfirstlane(r.L);
   r.s = __builtin_amdgcn_readfirstlane(r.s);
   r.span = __builtin_amdgcn_readfirstlane(r.span);
   r.cls = __builtin_amdgcn_readfirstlane(r.cls);
-  return r;
+  m.trow = __builtin_amdgcn_readfirstlane((kPaged && p.table_rows) ? tr : (int32_t)b);
+  m.tstart = __builtin_amdgcn_readfirstlane((kPaged && p.table_starts) ? ts : 0);
+  m.offset = __builtin_amdgcn_readfirstlane(kPaged ? 0 : of);
+  m.split = hp && pm == kPlanMagic && pr == p.num_rows && r.cls == kClassLong && ps >= 2 &&
+            ps == segments_for(r.span) && pl >= 0 && pl < plan_split_cap(p.num_rows);
+  return m;
+}
+
+// row_emit from words already loaded.
+template <bool kPaged>
+__device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b, const RowMeta& m) {
+  Emit<kPaged> em;
+  em.out = p.out + b * p.k;
+  em.out_raw = nullptr;
+  em.page_bits = p.page_bits;
+  em.staged = false;
+  em.pt_first = 0;
+  em.pt_off = 0;
+  if constexpr (kPaged) {
+    em.pt = p.page_table + (int64_t)m.trow * p.pt_stride;
+    em.pt_off = m.tstart;
+    if (p.out_raw) em.out_raw = p.out_raw + b * p.k;
+    em.offset = 0;
+  } else {
+    em.pt = nullptr;
+    em.offset = m.offset;
+  }
+  return em;
 }
 
 __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const RowInfo& r) {
@@ -1398,26 +1482,15 @@ __device__ __forceinline__ bool plan_ok(const Params& p) {
   return p.plan && p.plan[kPlanWordMagic] == kPlanMagic && p.plan[kPlanWordRows] == p.num_rows;
 }
 
-// Workgroup b serves row b if the row is of class kClass, else nothing
-// (-1). Every kernel derives a row's class from its length and start, so
-// each row is served by exactly one kernel whatever the plan says; the
-// row's data is the first thing a workgroup loads, with no plan lookup
-// before it.
-template <int kClass>
-__device__ __forceinline__ int64_t class_row(const Params& p, RowInfo& r) {
-  (void)p;
-  const int64_t b = blockIdx.x;
-  r = group_row_info(p, b);
-  return r.cls == kClass ? b : -1;
-}
 
 // Trivial rows and spans <= 8192 floats, kept in registers.
 template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_short_kernel(const Params p) {
-  RowInfo r;
-  const int64_t b = class_row<kClassShort>(p, r);
-  if (b < 0) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const int64_t b = blockIdx.x;
+  const RowMeta m = row_meta<kPaged>(p, b, false);
+  const RowInfo& r = m.r;
+  if (r.cls != kClassShort) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial(em, r.L, p.k);
     return;
@@ -1431,10 +1504,11 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const Params p) {
 // sets the time.
 template <bool kPaged>
 __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
-  RowInfo r;
-  const int64_t b = class_row<kClassShort>(p, r);
-  if (b < 0) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const int64_t b = blockIdx.x;
+  const RowMeta m = row_meta<kPaged>(p, b, false);
+  const RowInfo& r = m.r;
+  if (r.cls != kClassShort) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial<kPaged, kWideBlock>(em, r.L, p.k);
     return;
@@ -1451,9 +1525,10 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
 template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
   const int64_t b = blockIdx.x;
-  const RowInfo r = group_row_info(p, b);
+  const RowMeta m = row_meta<kPaged>(p, b, false);
+  const RowInfo& r = m.r;
   if (r.cls != kClassShort && r.cls != kClassMid) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial(em, r.L, p.k);
     return;
@@ -1476,9 +1551,10 @@ template <bool kPaged>
 __global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) void
 rows_reg_kernel(const Params p) {
   const int64_t b = blockIdx.x;
-  const RowInfo r = group_row_info(p, b);
+  const RowMeta m = row_meta<kPaged>(p, b, false);
+  const RowInfo& r = m.r;
   if (r.cls == kClassLong) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial<kPaged, kBigBlock>(em, r.L, p.k);
     return;
@@ -1508,9 +1584,10 @@ template <bool kPaged>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
 rows_long_kernel(const Params p) {
   const int64_t b = blockIdx.x;
-  const RowInfo r = group_row_info(p, b);
-  if (r.cls != kClassLong || split_served(p, b, r)) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const RowMeta m = row_meta<kPaged>(p, b, true);
+  const RowInfo& r = m.r;
+  if (r.cls != kClassLong || m.split) return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial<kPaged, kLongBlock>(em, r.L, p.k);
     return;

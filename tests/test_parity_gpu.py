@@ -82,6 +82,12 @@ def _edge_rows(k):
                 rows.append((L, r, pat))
     rows += [(131072, 1, "fp16"), (131072, 3, "equal"), (131072, 0, "alphabet"),
              (131072, 2, "normal")]
+    # streamed rows whose largest keys crowd the first columns (the list's
+    # opening threshold is then above the k-th key: two-pass re-read), rise
+    # along the row (the list fills and is compacted again and again), or
+    # are all -inf
+    rows += [(131072, 2, "decreasing"), (40000, 3, "decreasing"), (131072, 0, "increasing"),
+             (65537, 1, "neg_inf")]
     return rows
 
 
