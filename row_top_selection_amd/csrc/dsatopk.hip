@@ -1417,8 +1417,11 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   const int32_t* a_pr = hp ? p.plan + kPlanWordRows : a_len;
   const int32_t* a_ps = hp ? p.plan + plan_nseg_word(p.num_rows) + b : a_len;
   const int32_t* a_pl = hp ? p.plan + plan_slot_word(p.num_rows) + b : a_len;
-  int32_t len = *a_len, rs = *a_rs, tr = *a_tr, ts = *a_ts, of = *a_of;
-  int32_t pm = *a_pm, pr = *a_pr, ps = *a_ps, pl = *a_pl;
+  // (readfirstlane: a no-op on scalar loads; a vector load, where the
+  // compiler cannot prove the words unchanged, still ends in an SGPR)
+  auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(*a); };
+  int32_t len = rd(a_len), rs = rd(a_rs), tr = rd(a_tr), ts = rd(a_ts), of = rd(a_of);
+  int32_t pm = rd(a_pm), pr = rd(a_pr), ps = rd(a_ps), pl = rd(a_pl);
   // every value is needed here: the compiler may not sink a load into the
   // branch that uses it (which would put it behind another load's wait)
   asm volatile("" : "+s"(len), "+s"(rs), "+s"(tr), "+s"(ts), "+s"(of), "+s"(pm), "+s"(pr),
