@@ -1082,10 +1082,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   const __amdgpu_buffer_rsrc_t rs = row_buffer(rv.base4, nvec);
   const int32_t off = t * 16;
   if (t < 4) sm.ccnt[t] = 0;
-  if (t == 0) {
-    sm.n0 = 0;
-    sm.bcast[3] = 0;  // the final cut's count of saturated offsets
-  }
+  if (t == 0) sm.n0 = 0;
   uint32_t T = 1;
   uint32_t n = 0;
   float4 buf[kS1Depth];
@@ -1261,11 +1258,11 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // holds keys below every threshold, i.e. all-ones NaNs): two passes
   if (overflow || n < (uint32_t)k) return false;
 
-  // The cut and the stage run on the list where it stands. On offsets above
-  // T when fewer than the kk taken pairs reach the offset bound (those are
-  // then all above the cut, where their order does not matter); on the keys
-  // themselves otherwise.
-  const uint32_t kk = n < (uint32_t)k ? n : (uint32_t)k;
+  // The cut and the stage run on the list where it stands (at least k
+  // pairs). On offsets above T when fewer than k pairs reach the offset
+  // bound (those are then all above the cut, where their order does not
+  // matter); on the keys themselves otherwise.
+  const uint32_t kk = (uint32_t)k;
   // The row's page-table entries, when at most kBins - kMaxK, into registers
   // now (their loads overlap the cut), and into the histogram's upper part
   // once the cut is found: the stage below it takes at most kMaxK words.
@@ -1284,31 +1281,28 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
       tv[q] = e < tsp.y ? em.pt[tsp.x + e] : 0;
     }
   }
-  {
-    uint32_t sat = 0;
-    for (uint32_t i = (uint32_t)tix(); i < n; i += BS)
-      sat += (uint32_t)__builtin_popcountll(
-          __ballot(sm.cand[i].x - T >= ListSrc<BS>::kSat));
-    if (lane_id() == 0 && sat) atomicAdd(&sm.bcast[3], sat);
-  }
   clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
   int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  // fewer than k pairs only if the window holds keys below every
-  // threshold, i.e. all-ones NaNs
-  if (kk == 0) {
-    for (int32_t i = tix(); i < k; i += BS) stage[i] = -1;
-    __syncthreads();
-    write_stage<kPaged, BS>(em, stage, rv.span - rv.rem, k, nullptr);
-    return true;
-  }
-  const bool offsets = __builtin_amdgcn_readfirstlane(sm.bcast[3]) < kk;
-  const ListSrc<BS> src{sm.cand, n, T, offsets};
+  // Level 1 on the offsets first: every offset at the bound lands in the
+  // top bin (with the offsets just below it), so a top bin of fewer than
+  // k pairs means fewer than k at the bound. Otherwise (keys far above T)
+  // the histogram is rebuilt on the keys.
+  const uint32_t one = opaque_one();
   {
-    const uint32_t one = opaque_one();
-    src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
+    const ListSrc<BS> so{sm.cand, n, T, true};
+    so.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
   }
   __syncthreads();
+  const bool offsets = __builtin_amdgcn_readfirstlane(sm.hist[kBins - 1]) < kk;
+  const ListSrc<BS> src{sm.cand, n, T, offsets};
+  if (!offsets) {
+    __syncthreads();  // every wave has read the top bin
+    clear_bins<kBins, BS>(sm.hist);
+    __syncthreads();
+    src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
+    __syncthreads();
+  }
   const Cut cut = refine_in_registers<BS>(src, sm, kk, offsets);
   // every search of the cut ended with a barrier after its last histogram
   // read; the tie ranking reads only the first 64 words
