@@ -265,6 +265,21 @@ constexpr int kLongBlock = 1024;
 // compaction about 2000 pairs of room stay above k + one chunk, so on rows
 // in random order the list is compacted a handful of times per row.
 constexpr int kS1Chunk = 4 * kLongBlock;
+
+// The opening chunks of the streamed row that is likely to start next on
+// this workgroup's CU: two streaming workgroups per CU on a 256-CU part
+// run rows b .. b + 511 at once, and workgroups start in row order, so row
+// b + 512 follows about when row b ends (its XCD is row b's: workgroups go
+// to the XCDs round-robin). A streamed row touches one word per 64-byte
+// line of that row's first 16384 columns during its own final cut, with
+// the default cache policy, so the next row's first loads find them in the
+// caches instead of waiting a full HBM round trip under load. A guess only
+// about timing: every row is still read by its own workgroup.
+constexpr int kPrefetchAhead = 512;
+struct Prefetch {
+  const float* base;  // first aligned column of the row's window, or null
+  int32_t bytes;      // bytes to touch from base
+};
 constexpr int kS1Depth = 4;
 constexpr int kS1Cap = 8160;
 
@@ -1074,7 +1089,7 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
 
 template <bool kPaged, int BS>
 __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const Emit<kPaged>& em,
-                                            SmemS1& sm, SmemRegB<BS>& fin) {
+                                            SmemS1& sm, SmemRegB<BS>& fin, const Prefetch pf) {
   static_assert(kS1Chunk == 4 * BS, "one float4 per thread per chunk");
   const int t = tix();
   const int32_t nvec = (rv.span + 3) >> 2;
@@ -1257,6 +1272,14 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // fewer than k pairs: T opened above the span's k-th key (or the window
   // holds keys below every threshold, i.e. all-ones NaNs): two passes
   if (overflow || n < (uint32_t)k) return false;
+  // the next row's opening lines (see kPrefetchAhead): one word per 64-byte
+  // line, loads past pf.bytes return zero without touching memory
+  uint32_t touched = 0;
+  if (pf.base) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(pf.base), (short)0, pf.bytes, 0x00020000);
+    touched = __builtin_amdgcn_raw_buffer_load_b32(r, tix() * 64, 0, 0);
+  }
 
   // The cut and the stage run on the list where it stands (at least k
   // pairs). On offsets above T when fewer than k pairs reach the offset
@@ -1335,6 +1358,7 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   for (int32_t i = (int32_t)kk + tix(); i < k; i += BS) stage[i] = -1;
   __syncthreads();
   write_stage<kPaged, BS>(et, stage, L, k, table);
+  asm volatile("" ::"v"(touched));  // keeps the touch (landed long before)
   return true;
 }
 
@@ -1595,7 +1619,19 @@ rows_long_kernel(const Params p) {
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
-  if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin)) {
+  Prefetch pf{nullptr, 0};
+  if (b + kPrefetchAhead < p.num_rows) {
+    const int64_t b2 = b + kPrefetchAhead;
+    const int32_t l2 = __builtin_amdgcn_readfirstlane(p.seq_lens[b2]);
+    const int32_t s2 = p.row_starts ? __builtin_amdgcn_readfirstlane(p.row_starts[b2]) : 0;
+    const int32_t L2 = l2 < 0 ? 0 : (l2 > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : l2);
+    const int32_t span2 = L2 + (s2 & 3);
+    if (L2 > p.k && span2 > kBigVec * 4 * kBigBlock) {
+      pf.base = p.scores + b2 * p.stride + (s2 - (s2 & 3));
+      pf.bytes = 4 * (span2 < kS1Depth * kS1Chunk ? span2 : kS1Depth * kS1Chunk);
+    }
+  }
+  if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
     __syncthreads();
     row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
   }
