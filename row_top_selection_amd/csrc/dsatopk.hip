@@ -1487,6 +1487,30 @@ __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b, con
   return em;
 }
 
+// The row `ahead` rows on, when it is a row with more than k elements and
+// a span in (lo, hi]: its first `cap` floats from the aligned column at or
+// below its start (see kPrefetchAhead for the idea: the workgroups in
+// flight serve `ahead` consecutive rows, so that row starts on this
+// workgroup's XCD about when this one ends). Streamed rows only: touching
+// the next rows of the 8192-float register kernel (2048 rows ahead, 64 MiB
+// of lines against 32 MiB of L2) made its launches half as slow again.
+__device__ __forceinline__ Prefetch next_row(const Params& p, int64_t b, int32_t ahead,
+                                             int32_t lo, int32_t hi, int32_t cap) {
+  Prefetch pf{nullptr, 0};
+  if (b + ahead < p.num_rows) {
+    const int64_t b2 = b + ahead;
+    const int32_t l2 = __builtin_amdgcn_readfirstlane(p.seq_lens[b2]);
+    const int32_t s2 = p.row_starts ? __builtin_amdgcn_readfirstlane(p.row_starts[b2]) : 0;
+    const int32_t L2 = l2 < 0 ? 0 : (l2 > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : l2);
+    const int32_t span2 = L2 + (s2 & 3);
+    if (L2 > p.k && span2 > lo && span2 <= hi) {
+      pf.base = p.scores + b2 * p.stride + (s2 - (s2 & 3));
+      pf.bytes = 4 * (span2 < cap ? span2 : cap);
+    }
+  }
+  return pf;
+}
+
 __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const RowInfo& r) {
   RowView rv;
   const int32_t rem = r.s & 3;
@@ -1619,18 +1643,8 @@ rows_long_kernel(const Params p) {
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
-  Prefetch pf{nullptr, 0};
-  if (b + kPrefetchAhead < p.num_rows) {
-    const int64_t b2 = b + kPrefetchAhead;
-    const int32_t l2 = __builtin_amdgcn_readfirstlane(p.seq_lens[b2]);
-    const int32_t s2 = p.row_starts ? __builtin_amdgcn_readfirstlane(p.row_starts[b2]) : 0;
-    const int32_t L2 = l2 < 0 ? 0 : (l2 > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : l2);
-    const int32_t span2 = L2 + (s2 & 3);
-    if (L2 > p.k && span2 > kBigVec * 4 * kBigBlock) {
-      pf.base = p.scores + b2 * p.stride + (s2 - (s2 & 3));
-      pf.bytes = 4 * (span2 < kS1Depth * kS1Chunk ? span2 : kS1Depth * kS1Chunk);
-    }
-  }
+  const Prefetch pf = next_row(p, b, kPrefetchAhead, kBigVec * 4 * kBigBlock,
+                               DSATOPK_MAX_SEQ_LEN + 3, kS1Depth * kS1Chunk);
   if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
     __syncthreads();
     row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
