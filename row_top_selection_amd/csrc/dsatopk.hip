@@ -281,6 +281,7 @@ struct Prefetch {
   int32_t bytes;      // bytes to touch from base
 };
 constexpr int kS1Depth = 4;
+constexpr int kS1Sample = 2;  // chunks whose histogram sets the list's opening threshold
 constexpr int kS1Cap = 8160;
 
 // The list's length lives in registers, never in one shared counter that
@@ -1161,7 +1162,8 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
           const uint64_t mm = m[e][q];
           const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
               (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
-          if ((mm >> lane_id()) & 1ull)
+          // slots past the list are dropped; the caller sees n > kS1Cap
+          if (((mm >> lane_id()) & 1ull) && base + rank < (uint32_t)kS1Cap)
             sm.cand[base + rank] =
                 make_uint2(wk[d][q], (uint32_t)((d * BS + t) * 4 + q - rv.rem));
           base += (uint32_t)__builtin_popcountll(mm);
@@ -1174,11 +1176,14 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   for (int d = 0; d < kS1Depth; ++d) issue(buf[d], d);
 
   // Warm start: the first kS1Depth chunks (16384 elements; a long span has
-  // more) are a register row. T opens at the lowest key of the level-1 bin
-  // that holds the kt-th largest key of this subset, and every subset pair
-  // at or above it opens the list, with kt the count that, at the subset's
-  // rate, puts about 1.5 k keys of the whole span at or above the kt-th key
-  // (the rest of the bin adds a few hundred on N(0,1) rows). On rows whose large keys are spread along the
+  // more) are held as keys. T opens at the lowest key of the level-1 bin
+  // that holds the kt-th largest key of the first kS1Sample chunks, and
+  // every pair of the kS1Depth chunks at or above it opens the list, with
+  // kt the count that, at the sample's rate, puts about 1.25 k keys of the
+  // whole span at or above the kt-th key (the rest of the bin adds a fifth
+  // or more on N(0,1) rows: about 1.5 k in all). Histogramming half the
+  // held chunks took 2-3 % off streamed launches; kt is then 320 (65536
+  // columns) or 160 (131072). On rows whose large keys are spread along the
   // span the list then never reaches the compaction mark (opening at the
   // subset's k-th key, the list of a 131072-column row took about 4000
   // appends and two compactions). A span where fewer than k keys reach T
@@ -1204,22 +1209,34 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     {
       const uint32_t one = opaque_one();
 #pragma unroll
-      for (int d = 0; d < kS1Depth; ++d)
+      for (int d = 0; d < kS1Sample; ++d)
 #pragma unroll
         for (int q = 0; q < 4; ++q) lds_add(&fin.hist[wk[d][q] >> 20], one);
     }
     __syncthreads();
-    constexpr int32_t kWarm = kS1Depth * kS1Chunk;
+    constexpr int32_t kWarm = kS1Sample * kS1Chunk;
     const uint32_t kt = (uint32_t)min(
-        k, max(1, (int32_t)((3 * k * kWarm + 2 * rv.span - 1) / (2 * rv.span))));
+        k, max(1, (int32_t)((5 * k * kWarm + 4 * rv.span - 1) / (4 * rv.span))));
     const BinHit h = group_find<kBins, true, BS>(fin.hist, kt, fin);
     uint32_t tau;
+    // (the sample's pairs at or above T fit; the other held chunks' pairs
+    // are checked against the list's size after the append)
     if (h.before + h.cnt <= (uint32_t)(kS1Cap - kS1Chunk)) {
       // the search closed with a barrier: nothing reads the final-cut space
       tau = h.bin << 20;
       tau = tau ? tau : 1u;
       append_all(wk, [tau](uint32_t kv, int32_t) { return kv >= tau; });
     } else {
+      // the held chunks past the sample join the histogram (every wave is
+      // past the search's closing barrier): the exact cut of all of them
+      {
+        const uint32_t one = opaque_one();
+#pragma unroll
+        for (int d = kS1Sample; d < kS1Depth; ++d)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lds_add(&fin.hist[wk[d][q] >> 20], one);
+      }
+      __syncthreads();
       const RegSrc<kS1Depth, BS> src{wk, -rv.rem, kS1Depth - 1};
       const Cut cut = refine_in_registers<BS>(src, fin, (uint32_t)k);
       __syncthreads();  // the final-cut space aliases the list
@@ -1244,7 +1261,10 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
   // reason every buffered chunk is processed and refilled (chunks past the
   // row are all masked, and loads past the buffer's end return zeros
   // without touching memory).
-  bool overflow = false;
+  // The sample bounds only its own chunks' pairs: when the held chunks
+  // brought more pairs than the list holds (keys rising along the row),
+  // some were dropped and the row takes the two-pass path.
+  bool overflow = n > (uint32_t)kS1Cap;
   for (int32_t c0 = kS1Depth; c0 < nchunk && !overflow; c0 += kS1Depth) {
 #pragma unroll
     for (int d = 0; d < kS1Depth; ++d) {

@@ -84,10 +84,11 @@ def _edge_rows(k):
              (131072, 2, "normal")]
     # streamed rows whose largest keys crowd the first columns (the list's
     # opening threshold is then above the k-th key: two-pass re-read), rise
-    # along the row (the list fills and is compacted again and again), or
-    # are all -inf
+    # along the row (the list fills and is compacted again and again), are
+    # all -inf, or rise over the first 16384 columns only (more pairs reach
+    # the opening threshold than the list holds)
     rows += [(131072, 2, "decreasing"), (40000, 3, "decreasing"), (131072, 0, "increasing"),
-             (65537, 1, "neg_inf")]
+             (65537, 1, "neg_inf"), (131072, 1, "rising_head"), (65536, 3, "rising_head")]
     return rows
 
 

@@ -11,7 +11,7 @@ import numpy as np
 from .configs import OUTSIDE_SCORE, PAGE_SIZE, Problem, random_page_tables
 
 PATTERNS = ("normal", "fp16", "alphabet", "equal", "neg_inf", "increasing", "decreasing",
-            "zeros_mixed", "one_pos_inf")
+            "zeros_mixed", "one_pos_inf", "rising_head")
 
 _ALPHABET = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.0, np.inf], dtype=np.float32)
 
@@ -50,6 +50,14 @@ def _values(rng, pattern, L: int) -> np.ndarray:
     if pattern == "zeros_mixed":
         v = rng.choice(np.array([-0.0, 0.0], dtype=np.float32), size=L)
         v[rng.integers(0, L, size=max(1, L // 100))] = 1.0
+        return v
+    if pattern == "rising_head":
+        # rising over the first 16384 positions, low noise after them: a
+        # long row's largest keys all sit in its first 16384 columns, and
+        # the largest of those at their end
+        h = min(L, 16384)
+        v = np.float32(-2.0) + np.float32(0.1) * rng.standard_normal(L, dtype=np.float32)
+        v[:h] = np.linspace(-3.0, 3.0, h, dtype=np.float32)
         return v
     if pattern == "one_pos_inf":
         v = np.full(L, -np.inf, dtype=np.float32)
