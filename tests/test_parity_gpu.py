@@ -315,6 +315,39 @@ def test_sustained_launch_sampled_rows(orc, name):
     assert (words[12] == n) == (n <= SPLIT_CAP)
 
 
+@pytest.mark.parametrize("k", [2048, 1000])
+def test_streamed_ragged_rows_with_starts(orc, k):
+    """A RAGGED launch of 640 rows: streamed rows with starts of every
+    residue, every fifth row a register row. Streamed rows read the opening
+    lines of the row 512 on (those rows' windows start anywhere, and some of
+    them are not streamed); no plan, so every long row is streamed. 48
+    sampled rows, half of them past row 512, against the oracle."""
+    import torch
+
+    import row_top_selection_amd as dt
+    from workloads.configs import OUTSIDE_SCORE, Problem
+
+    rng = np.random.default_rng(20261202 + k)
+    R, stride = 640, 131072 + 16
+    starts = rng.integers(0, 16, size=R).astype(np.int32)
+    lens = rng.integers(32769, 131072 - 15, size=R).astype(np.int32)
+    lens[::5] = rng.integers(k + 1, 16384, size=len(lens[::5]))
+    scores = np.full((R, stride), OUTSIDE_SCORE, dtype=np.float32)
+    for b in range(R):
+        scores[b, starts[b]:starts[b] + lens[b]] = rng.standard_normal(lens[b], dtype=np.float32)
+    offs = rng.integers(0, 1 << 20, size=R).astype(np.int32)
+    p = Problem(f"streamed_ragged_k{k}", "ragged", k, scores, lens, row_starts=starts,
+                out_offsets=offs)
+    print(f"[gpu] {p.name} rows={R}", flush=True)
+    d = gpu_run.to_dev(p)
+    rows = np.unique(np.concatenate([rng.choice(512, 24, replace=False),
+                                     512 + rng.choice(R - 512, 24, replace=False)]))
+    want = orc.ragged(scores[rows], lens[rows], starts[rows], offs[rows], k)
+    out = dt.ragged(d["scores"], d["lens"], d["offs"], k, row_starts=d["starts"])
+    got = out[torch.from_numpy(rows).to(out.device)].cpu().numpy()
+    assert_rows_equal(canonical(got, lens[rows], k), want, p.name)
+
+
 PACKED = [
     # (id, query rows per request, KV columns per request, k, largest window shift)
     ("mixed_classes", [5, 2, 9], 20000, 2048, 999),
