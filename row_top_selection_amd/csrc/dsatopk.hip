@@ -232,8 +232,8 @@ struct SmemRegB {
   uint32_t wave_cnt[BS / 64];  // per wave: selected elements
   uint32_t bcast[4];           // a bin search's result, when one wave searches
   // per-lane and per-wave running sums of a search shared by all waves
-  // (1024-thread workgroups only)
-  uint32_t lsum[BS > kBlock ? BS : 1];
+  // (register-row layouts of 256 threads and more)
+  uint32_t lsum[BS >= kBlock ? BS : 1];
   uint32_t wsum[BS / 64];
   uint32_t tie_n;  // slots taken by a small tie class's positions
 };
@@ -541,9 +541,8 @@ __device__ __forceinline__ void write_stage(const Emit<kPaged>& em, const int32_
 }
 
 // A bin search whose result every thread needs: wave 0 searches and the
-// result goes through LDS (one barrier). Several workgroups share a CU, so
-// the issue slots of the idle waves are not lost, while a search by every
-// wave would multiply its VALU work by the wave count.
+// result goes through LDS (one barrier). Used where a layout holds no
+// all-wave running sums (the streaming list's compactions, small digits).
 template <int NB, bool kDesc, class Sm>
 __device__ __forceinline__ BinHit wave0_find(const uint32_t* hist, uint32_t need, Sm& sm) {
   if (wave_id() == 0) {
@@ -614,19 +613,24 @@ __device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t 
 }
 
 // Whether a shared-memory layout holds the running sums of an all-wave
-// search (the 1024-thread register-row layouts do).
+// search (the register-row layouts do). Register rows search their
+// 4096-bin digits with every wave: the rows are latency-bound, not
+// VALU-bound, and the search by wave 0 alone kept a 256-thread row's cut
+// at 38 % of its workgroup's life (8192-float rows: 232 -> 216 us per
+// 32768-row launch; 16384-float rows: 211 -> 201 us, at one workgroup
+// per CU fewer for the VGPRs the search adds).
 template <class Sm>
 struct HasWaveSums {
   static constexpr bool value = false;
 };
 template <int BS>
 struct HasWaveSums<SmemRegB<BS>> {
-  static constexpr bool value = BS > kBlock;
+  static constexpr bool value = BS >= kBlock;
 };
 
 template <int NB, bool kDesc, int BS, class Sm>
 __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, Sm& sm) {
-  if constexpr (BS > kBlock && NB >= 4 * BS && HasWaveSums<Sm>::value)
+  if constexpr (BS >= kBlock && NB >= 4 * BS && HasWaveSums<Sm>::value)
     return all_waves_find<NB, kDesc, BS>(hist, need, sm);
   else
     return wave0_find<NB, kDesc>(hist, need, sm);
@@ -1585,7 +1589,7 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
 
 // Every row of a batch with a score stride of 8193 .. 16384 floats, in one
 // launch: 256 threads per row, holding 8 or 16 float4 each by the row's
-// span. Six rows share a CU (77 VGPRs); 512 threads with 8 float4 each
+// span. Five rows share a CU (86 VGPRs); 512 threads with 8 float4 each
 // (three rows per CU) ran 6-12% slower on such rows.
 template <bool kPaged>
 __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
