@@ -267,7 +267,7 @@ constexpr int kLongBlock = 1024;
 constexpr int kS1Chunk = 4 * kLongBlock;
 
 // The opening chunks of the streamed row that is likely to start next on
-// this workgroup's CU: two streaming workgroups per CU on a 256-CU part
+// this workgroup's XCD: two streaming workgroups per CU on a 256-CU part
 // run rows b .. b + 511 at once, and workgroups start in row order, so row
 // b + 512 follows about when row b ends (its XCD is row b's: workgroups go
 // to the XCDs round-robin). A streamed row touches one word per 64-byte
@@ -1023,9 +1023,9 @@ __device__ __forceinline__ void row_streaming(const RowView& rv, int32_t k, cons
 // at least k pairs reached T, every pair the row's top k needs is in the
 // list. After the last chunk the register path resolves the exact cut over
 // the list (ties included) and emits. Returns false, having written
-// nothing, when ties keep the list too full to take another chunk or when
-// fewer than k keys of the row reached T; the caller then runs the
-// two-pass path.
+// nothing, when the opening pairs overflow the list, when ties keep the
+// list too full to take another chunk, or when fewer than k keys of the
+// row reached T; the caller then runs the two-pass path.
 // From per-wave counts cnt[0 .. W) (written before a barrier the caller
 // has passed): x = the count of the waves before this one, y = the total.
 template <int W>
@@ -1415,20 +1415,25 @@ struct RowInfo {
   int32_t cls;
 };
 
-// Class of a row: short = trivial (L <= k) or span <= 8192 floats; mid =
-// span <= 16384; big = span <= 32768; long = the rest.
-__device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32_t* row_starts,
-                                            int32_t k, int64_t b) {
+// Class of a row from its length word and start: short = trivial (L <= k)
+// or span <= 8192 floats; mid = span <= 16384; big = span <= 32768; long =
+// the rest. The one rule every kernel, the plan and the next-row touch use,
+// so that each row is served by exactly one kernel.
+__device__ __forceinline__ RowInfo classify(int32_t len, int32_t s, int32_t k) {
   RowInfo r;
-  int32_t L = seq_lens[b];
-  r.L = L < 0 ? 0 : (L > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : L);
-  r.s = row_starts ? row_starts[b] : 0;
+  r.L = len < 0 ? 0 : (len > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : len);
+  r.s = s;
   r.span = r.L + (r.s & 3);
   r.cls = (r.L <= k || r.span <= kSmallVec * 4 * kBlock) ? kClassShort
           : (r.span <= kLargeVec * 4 * kBlock)            ? kClassMid
           : (r.span <= kBigVec * 4 * kBigBlock)           ? kClassBig
                                                           : kClassLong;
   return r;
+}
+
+__device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32_t* row_starts,
+                                            int32_t k, int64_t b) {
+  return classify(seq_lens[b], row_starts ? row_starts[b] : 0, k);
 }
 
 // Every word a row's workgroup reads before its scores, loaded together:
@@ -1470,13 +1475,7 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
                "+s"(ps), "+s"(pl));
   RowMeta m;
   RowInfo& r = m.r;
-  r.L = len < 0 ? 0 : (len > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : len);
-  r.s = p.row_starts ? rs : 0;
-  r.span = r.L + (r.s & 3);
-  r.cls = (r.L <= p.k || r.span <= kSmallVec * 4 * kBlock) ? kClassShort
-          : (r.span <= kLargeVec * 4 * kBlock)              ? kClassMid
-          : (r.span <= kBigVec * 4 * kBigBlock)             ? kClassBig
-                                                            : kClassLong;
+  r = classify(len, p.row_starts ? rs : 0, p.k);
   r.L = __builtin_amdgcn_readfirstlane(r.L);
   r.s = __builtin_amdgcn_readfirstlane(r.s);
   r.span = __builtin_amdgcn_readfirstlane(r.span);
@@ -1511,25 +1510,24 @@ __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b, con
   return em;
 }
 
-// The row `ahead` rows on, when it is a row with more than k elements and
-// a span in (lo, hi]: its first `cap` floats from the aligned column at or
-// below its start (see kPrefetchAhead for the idea: the workgroups in
-// flight serve `ahead` consecutive rows, so that row starts on this
-// workgroup's XCD about when this one ends). Streamed rows only: touching
-// the next rows of the 8192-float register kernel (2048 rows ahead, 64 MiB
-// of lines against 32 MiB of L2) made its launches half as slow again.
+// The row `ahead` rows on, when it is of class `cls`: its first `cap`
+// floats from the aligned column at or below its start (see kPrefetchAhead
+// for the idea: the workgroups in flight serve `ahead` consecutive rows, so
+// that row starts on this workgroup's XCD about when this one ends).
+// Streamed rows only: touching the next rows of the 8192-float register
+// kernel (2048 rows ahead, 64 MiB of lines against 32 MiB of L2) made its
+// launches half as slow again.
 __device__ __forceinline__ Prefetch next_row(const Params& p, int64_t b, int32_t ahead,
-                                             int32_t lo, int32_t hi, int32_t cap) {
+                                             int32_t cls, int32_t cap) {
   Prefetch pf{nullptr, 0};
   if (b + ahead < p.num_rows) {
     const int64_t b2 = b + ahead;
     const int32_t l2 = __builtin_amdgcn_readfirstlane(p.seq_lens[b2]);
     const int32_t s2 = p.row_starts ? __builtin_amdgcn_readfirstlane(p.row_starts[b2]) : 0;
-    const int32_t L2 = l2 < 0 ? 0 : (l2 > DSATOPK_MAX_SEQ_LEN ? DSATOPK_MAX_SEQ_LEN : l2);
-    const int32_t span2 = L2 + (s2 & 3);
-    if (L2 > p.k && span2 > lo && span2 <= hi) {
+    const RowInfo r2 = classify(l2, s2, p.k);
+    if (r2.cls == cls) {
       pf.base = p.scores + b2 * p.stride + (s2 - (s2 & 3));
-      pf.bytes = 4 * (span2 < cap ? span2 : cap);
+      pf.bytes = 4 * (r2.span < cap ? r2.span : cap);
     }
   }
   return pf;
@@ -1667,8 +1665,7 @@ rows_long_kernel(const Params p) {
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
-  const Prefetch pf = next_row(p, b, kPrefetchAhead, kBigVec * 4 * kBigBlock,
-                               DSATOPK_MAX_SEQ_LEN + 3, kS1Depth * kS1Chunk);
+  const Prefetch pf = next_row(p, b, kPrefetchAhead, kClassLong, kS1Depth * kS1Chunk);
   if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
     __syncthreads();
     row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
