@@ -312,20 +312,19 @@ def describe(p) -> dict:
             "seq_len": int(L[0]) if (L == L[0]).all() else [int(L.min()), int(L.max())]}
 
 
-SUSTAINED = {
-    "paged_decode_x32768": lambda w: w.scaled_decode(32768),
-    "paged_L16384_x16384": lambda w: w.scaled_paged(16384, 16384),
-    "paged_L32768_x8192": lambda w: w.scaled_paged(32768, 8192),
-    "paged_L65536_x4096": lambda w: w.scaled_paged(65536, 4096),
-    "paged_long_x2048": lambda w: w.scaled_long(2048),
-}
+def sustained_makers():
+    import workloads
+
+    return {workloads.sustained_name(L): (lambda L=L: workloads.sustained(L))
+            for L in workloads.SUSTAINED_LENGTHS}
 
 
 def only_workload(name: str):
     import workloads
 
-    if name in SUSTAINED:
-        return SUSTAINED[name](workloads)
+    sus = sustained_makers()
+    if name in sus:
+        return sus[name]()
     if name == "all_trivial":
         return workloads.all_trivial()
     return workloads.make_workload(name)
@@ -430,9 +429,9 @@ def main(argv=None):
         # paged decode rows from 8192 to 131072 columns, 1 GiB of scores per
         # launch (the decode and long-context shapes, and three between)
         sus = {}
-        for name, mk in SUSTAINED.items():
+        for name, mk in sustained_makers().items():
             # steady state: 0.1 s of untimed replays, then 5 x 20 launches
-            res = measure_workload(mk(workloads), 20, reps=5)
+            res = measure_workload(mk(), 20, reps=5)
             res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
             res["timing"] = f"mean of 5 replays of 20 launches after {SETTLE_S} s of replays"
             sus[name] = res

@@ -61,8 +61,9 @@ def test_many_rows_use_the_narrow_kernel(orc):
 @pytest.mark.parametrize("use_plan", [False, True])
 @pytest.mark.parametrize("mode", ["paged", "ragged"])
 def test_large_short_batch(orc, mode, use_plan):
-    """4096 short rows with mixed lengths and window offsets, trivial rows
-    among them, and fp16 ties: many workgroups of the short-row kernel."""
+    """4096 rows of spans up to 8192 floats in a score stride of 8196 (the
+    mid-stride kernel's 8-float4 rows), with mixed lengths and window
+    offsets, trivial rows among them, and fp16 ties."""
     p = workloads.short_mix(4096, mode)
     assert (p.seq_lens <= p.k).any() and (p.seq_lens > p.k).any()
     got = check(orc, p, use_plan, with_raw=False)
@@ -98,6 +99,64 @@ def _edge_rows(k):
 def test_edge_batch(orc, mode, k, use_plan):
     p = edge_batch(1000 + k, mode, k, _edge_rows(k), name=f"edge_{mode}_k{k}")
     check(orc, p, use_plan=use_plan, with_raw=not use_plan)
+
+
+# Score strides that select each register kernel (a row's span never exceeds
+# the stride): up to 8192 floats the short-row kernels (1024 threads per row
+# up to 512 rows, 256 threads above), up to 16384 the mid kernel (8 or 16
+# float4 per thread by the row's span).
+BANDS = {
+    "wide": (8192, 1),    # <= 512 rows: rows_wide_kernel
+    "short": (8192, 0),   # the rows repeated past 512 rows: rows_short_kernel
+    "mid": (16384, 1),    # spans on both sides of 8192: both mid-kernel branches
+}
+
+
+def _band_rows(k, stride):
+    """Every start residue; lengths -3, 0, 1, k-1, k, k+1 and the four spans
+    below the stride (plus, in the mid band, the spans around 8192); every
+    value pattern and tie classes of at most 64 and more than 64 elements at
+    a short and at the longest span."""
+    rows = []
+    for r in range(4):
+        top = [stride - r - d for d in range(4)]
+        mids = [8189 - r, 8192 - r, 8193 - r, 12000] if stride > 8192 else [4097]
+        for L in (-3, 0, 1, k - 1, k, k + 1, *mids, *top):
+            rows.append((L, r, "normal"))
+        for pat in PATTERNS:
+            for L in (3000, stride - r):
+                rows.append((L, r, pat))
+        for L in (3000, stride - r):
+            for tied, need in ((64, 1), (64, 37), (64, 63), (65, 40), (2, 1), (33, 17),
+                               (200, 150)):
+                if need <= k and k - need + tied <= L:
+                    rows.append((L, r, ("ties", k - need, tied)))
+    return rows
+
+
+@pytest.mark.parametrize("mode", ["ragged", "paged"])
+@pytest.mark.parametrize("k", [2048, 1000, 7, 1])
+@pytest.mark.parametrize("band", list(BANDS))
+def test_band_edges(orc, band, k, mode):
+    """The edge suite on the register kernels of short strides: the
+    1024-thread wide kernel (the paged decode kernel), the 256-thread short
+    kernel and both branches of the mid kernel, with trivial rows, every
+    start residue, signed zeros, infinities, equal rows and tie classes."""
+    stride, reps = BANDS[band]
+    rows = _band_rows(k, stride)
+    rows = rows * (reps or 512 // len(rows) + 1)
+    p = edge_batch(5000 + k + 7 * stride + reps, mode, k, rows, stride=stride,
+                   name=f"band_{band}_{mode}_k{k}")
+    assert p.stride == stride
+    assert (p.num_rows <= 512) == (band != "short")
+    check(orc, p, use_plan=False, with_raw=(mode == "paged"))
+
+
+def test_all_trivial_rows(orc):
+    """Every row's window fits in k: the trivial path alone, compared with
+    the oracle (the counter run shows that it reads no scores)."""
+    p = workloads.all_trivial()
+    check(orc, p, use_plan=True, with_raw=True)
 
 
 def _tie_rows(k):
@@ -279,24 +338,22 @@ def test_many_long_rows_are_streamed(orc):
     assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
 
 
-@pytest.mark.parametrize("name", ["paged_decode_x32768", "paged_L32768_x8192", "paged_L65536_x4096",
-                                  "paged_long_x2048", "paged_long_x256"])
-def test_sustained_launch_sampled_rows(orc, name):
+@pytest.mark.parametrize("L", list(workloads.SUSTAINED_LENGTHS) + ["split256"])
+def test_sustained_launch_sampled_rows(orc, L):
     """The launches the benchmark times for its sustained figures (about
-    1 GiB of scores: every CU serves several rounds of rows, and the waves
-    of a workgroup drift furthest apart), and the largest split batch (256
-    long rows, 4096 segments), three times with the plan; 40 sampled rows
-    against the oracle after each."""
+    1 GiB of scores at each window length from 8192 to 131072: every CU
+    serves several rounds of rows, and the waves of a workgroup drift
+    furthest apart), and the largest split batch (256 long rows, 4096
+    segments), three times with the plan; 40 sampled rows against the oracle
+    after each."""
     import torch
 
     import row_top_selection_amd as dt
 
-    makers = {"paged_decode_x32768": lambda: workloads.scaled_decode(32768),
-              "paged_L32768_x8192": lambda: workloads.scaled_paged(32768, 8192),
-              "paged_L65536_x4096": lambda: workloads.scaled_paged(65536, 4096),
-              "paged_long_x2048": lambda: workloads.scaled_long(2048),
-              "paged_long_x256": lambda: workloads.scaled_long(256)}
-    p = makers[name]()
+    if L == "split256":
+        name, p = "paged_long_x256", workloads.scaled_long(256)
+    else:
+        name, p = workloads.sustained_name(L), workloads.sustained(L)
     n = p.num_rows
     print(f"[gpu] {name} sustained launch", flush=True)
     d = gpu_run.to_dev(p)

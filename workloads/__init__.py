@@ -33,4 +33,8 @@ from .configs import (  # noqa: F401
     scaled_paged,
     short_mix,
     random_page_tables,
+    SUSTAINED_LENGTHS,
+    sustained,
+    sustained_name,
+    sustained_rows,
 )

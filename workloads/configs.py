@@ -212,6 +212,34 @@ def scaled_paged(L: int, rows: int, fp16: bool = False, seed: Optional[int] = No
     return Problem(f"paged_L{L}_x{rows}", "paged", 2048, scores, seq_lens, page_table=pt)
 
 
+# Sustained-rate launches: the paged decode row shape (N(0,1) fp32, k = 2048,
+# page size 64) at window lengths from 8192 to 131072, each with enough rows
+# for 1 GiB of scores per launch (131072: the fp16-rounded long-context rows).
+SUSTAINED_LENGTHS = (8192, 16384, 24576, 32768, 40960, 49152, 65536, 98304, 131072)
+
+
+def sustained_rows(L: int) -> int:
+    """Rows of a sustained launch of window length L: ceil(2^30 / (4 L))."""
+    return -(-(1 << 30) // (4 * L))
+
+
+def sustained_name(L: int) -> str:
+    if L == 8192:
+        return "paged_decode_x32768"
+    if L == 131072:
+        return "paged_long_x2048"
+    return f"paged_L{L}_x{sustained_rows(L)}"
+
+
+def sustained(L: int) -> Problem:
+    """The sustained launch of window length L (see SUSTAINED_LENGTHS)."""
+    if L == 8192:
+        return scaled_decode(sustained_rows(L))
+    if L == 131072:
+        return scaled_long(sustained_rows(L))
+    return scaled_paged(L, sustained_rows(L))
+
+
 def all_trivial(seed: Optional[int] = None) -> Problem:
     """128 PAGED rows whose windows all fit in k (L uniform in [1, 2048],
     k = 2048): every row takes the trivial path, so a launch should read no

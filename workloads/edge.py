@@ -67,18 +67,29 @@ def _values(rng, pattern, L: int) -> np.ndarray:
 
 
 def edge_batch(seed: int, mode: str, k: int, rows, page_size: int = PAGE_SIZE,
-               name: str = "edge") -> Problem:
+               name: str = "edge", stride: int = None) -> Problem:
     """``rows`` is a list of (seq_len, residue, pattern); negative seq_len allowed.
 
     row_start = 4 * (b % 3) + residue, so starts differ between rows; the
     score stride fits the longest window plus its start and is a multiple of 4.
+    With ``stride`` given, the score stride is exactly that (a multiple of 4)
+    and a row whose shifted window would not fit starts at its residue
+    instead; every window must then fit (residue + seq_len <= stride).
     """
     rng = np.random.default_rng(seed)
     R = len(rows)
     lens = np.array([r[0] for r in rows], dtype=np.int32)
     starts = np.array([4 * (b % 3) + r[1] for b, r in enumerate(rows)], dtype=np.int32)
-    need = int((starts.astype(np.int64) + np.maximum(lens, 0)).max()) if R else 4
-    stride = max(4, (need + 3) // 4 * 4)
+    if stride is not None:
+        assert stride % 4 == 0 and stride >= 4
+        res = np.array([r[1] for r in rows], dtype=np.int32)
+        spill = starts.astype(np.int64) + np.maximum(lens, 0) > stride
+        starts[spill] = res[spill]
+        assert (starts.astype(np.int64) + np.maximum(lens, 0) <= stride).all(), \
+            "a window does not fit the stride"
+    else:
+        need = int((starts.astype(np.int64) + np.maximum(lens, 0)).max()) if R else 4
+        stride = max(4, (need + 3) // 4 * 4)
     scores = np.full((R, stride), OUTSIDE_SCORE, dtype=np.float32)
     for b, (L, _, pattern) in enumerate(rows):
         if L > 0:
