@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-/* Status codes. */
+/* Status codes (every call returns one of these as an int). */
 enum {
     DSATOPK_OK = 0,
     /* k outside [1, DSATOPK_MAX_K]; num_rows < 0; a required pointer is NULL;
@@ -90,22 +90,32 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  * 16-byte aligned): each row's length class (trivial or up to 8192 aligned
  * floats, up to 16384, up to 32768, longer) with the rows of each class
  * listed, and, when the batch has at most 256 rows longer than 32768, a cut
- * of each of them
- * into segments of 8192 floats served by one workgroup each, with a zeroed
- * exchange area per row through which the segments merge their histograms
- * (with more long rows, each is streamed by one workgroup). Everything is computed on the
- * device; nothing is read back. The transform calls read only the split
- * schedule: rows of the other classes go to their kernel by their own
- * length, with no plan lookup before their data.
+ * of each of them into segments of 8192 floats (4096 when that would give
+ * fewer segments than the GPU's 256 CUs), served by one workgroup each,
+ * with a zeroed exchange area per row through which the segments merge
+ * their histograms. Longer rows of batches with more of them are read
+ * whole by one workgroup each. Everything is computed on the device;
+ * nothing is read back. The transform calls read only the split schedule:
+ * rows of the other classes go to their kernel by their own length, with no
+ * plan lookup before their data.
  *
  * The plan only schedules: a call given a plan built from different
  * seq_lens / row_starts / k, or no plan at all (NULL), returns the same
  * outputs (every kernel recomputes each row's class and segment count, and
- * a long row that does not match its planned segments is served by the
- * streaming long-row kernel). A plan must come from a dsatopk_plan call
- * with the same num_rows. A plan may be reused by any number of later
- * transform calls (one per layer, say): each call leaves the exchange areas
- * zeroed again. Calls that share one plan must not run concurrently.
+ * a long row that does not match its planned segments is read whole). A
+ * plan must come from a dsatopk_plan call with the same num_rows. A plan
+ * may be reused by any number of later transform calls (one per layer,
+ * say): each call leaves the exchange areas and its work counters zeroed
+ * again. Calls that share one plan must not run concurrently.
+ *
+ * Split rows wait for each other with bounded polls. A wait that gives up
+ * (which a correct launch never sees: it takes a segment that cannot run
+ * for about a second) sets the plan's error word (dsatopk_plan_error) and
+ * leaves that row's outputs all -1 instead of a partial selection; build
+ * the plan again before its next use. Plan word 15 (the int32 at byte
+ * offset 60) holds the number of polls after which such a wait gives up;
+ * dsatopk_plan writes 0, meaning about 2^20. It is exposed for tests that
+ * force a wait to give up.
  *
  * Source: PR #26788 digest, "Key source excerpts", plan_topk_v2 (a device
  * plan built from seq_lens and reused by the transform); the layout here is
@@ -113,14 +123,38 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  *
  * Errors: DSATOPK_ERR_INVALID_ARG (num_rows < 0, k outside [1, 2048],
  * NULL seq_lens or plan with num_rows > 0), DSATOPK_ERR_ALIGNMENT (plan not
- * 16-byte aligned), DSATOPK_ERR_PLAN_TOO_SMALL, DSATOPK_ERR_HIP.
+ * 16-byte aligned), DSATOPK_ERR_PLAN_TOO_SMALL, DSATOPK_ERR_HIP (a launch
+ * failed; its own status is checked, not an earlier one).
  * num_rows == 0 is a no-op.
  */
 int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num_rows, int32_t k,
                  void* plan, size_t plan_bytes, void* stream);
 
 /*
+ * dsatopk_plan_error - read a plan's error word.
+ *
+ * Copies the plan's error word into *error (host memory) after the work
+ * already queued on `stream` and synchronizes `stream`: 0 when no split-row
+ * wait of the transform calls since the plan was built gave up, 1 when one
+ * did (those rows' outputs are all -1; see dsatopk_plan). Unlike the other
+ * calls this one waits for the device and must not be captured in a graph.
+ * plan is a device pointer from dsatopk_plan, plan_bytes its size.
+ *
+ * Errors: DSATOPK_ERR_INVALID_ARG (NULL plan or error),
+ * DSATOPK_ERR_PLAN_TOO_SMALL (plan_bytes below the 256-byte header),
+ * DSATOPK_ERR_HIP (the copy or the synchronization failed).
+ */
+int dsatopk_plan_error(const void* plan, size_t plan_bytes, int32_t* error, void* stream);
+
+/*
  * dsatopk_paged - top-k with the PAGED emit.
+ *
+ * Source: PR #26788 digest ("faster top-k + page-table transform (runtime
+ * k <= 2048)"), "Key source excerpts": topk_transform_512_v2 takes the
+ * scores, seq_lens, the page tables, page_size and the plan and writes the
+ * page-mapped indices; PR #35175 digest, TopKProblem::transform_output (the
+ * map page_table[j >> page_bits] << page_bits | (j & (page_size - 1)), and
+ * -1 for padding).
  *
  *   scores            fp32 [num_rows, score_stride], row-major, 16-B aligned
  *                     base, score_stride % 4 == 0. Read only.

@@ -23,8 +23,8 @@ STATUS = {
     4: "DSATOPK_ERR_HIP",
 }
 
-EXPORTS = ("dsatopk_status_string", "dsatopk_plan_bytes", "dsatopk_plan", "dsatopk_paged",
-           "dsatopk_paged_packed", "dsatopk_ragged")
+EXPORTS = ("dsatopk_status_string", "dsatopk_plan_bytes", "dsatopk_plan", "dsatopk_plan_error",
+           "dsatopk_paged", "dsatopk_paged_packed", "dsatopk_ragged")
 
 
 class DsatopkError(RuntimeError):
@@ -50,12 +50,13 @@ def _lib():
         lib.dsatopk_plan_bytes.restype = sz
         lib.dsatopk_plan.argtypes = [P, P, i32, i32, P, sz, P]
         lib.dsatopk_plan.restype = ctypes.c_int
+        lib.dsatopk_plan_error.argtypes = [P, sz, P, P]
+        lib.dsatopk_plan_error.restype = ctypes.c_int
         lib.dsatopk_paged.argtypes = [P, i64, P, P, P, i64, i32, i32, i32, P, sz, P, P]
         lib.dsatopk_paged.restype = ctypes.c_int
         lib.dsatopk_paged_packed.argtypes = [P, i64, P, P, P, i64, i32, P, P, i32, i32, P, sz,
                                              P, P, P]
         lib.dsatopk_paged_packed.restype = ctypes.c_int
-        lib.dsatopk_paged.restype = ctypes.c_int
         lib.dsatopk_ragged.argtypes = [P, i64, P, P, P, i32, i32, P, sz, P, P]
         lib.dsatopk_ragged.restype = ctypes.c_int
         _handle = lib
@@ -81,7 +82,14 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _vec_i32(t, n, name):
+def _on(t, like, name):
+    """t must be a device tensor on like's device."""
+    if not t.is_cuda or t.device != like.device:
+        raise ValueError(f"{name} must be a device tensor on {like.device}")
+    return t
+
+
+def _vec_i32(t, n, name, like=None):
     import torch
 
     if t is None:
@@ -90,6 +98,8 @@ def _vec_i32(t, n, name):
         raise ValueError(f"{name} must be a contiguous int32 vector of length {n}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if like is not None:
+        _on(t, like, name)
     return t
 
 
@@ -103,14 +113,26 @@ def _scores(scores):
     return scores
 
 
-def _out(out, rows, k, like):
+def _out(out, rows, k, like, name="out"):
     import torch
 
     if out is None:
         return torch.empty((rows, k), dtype=torch.int32, device=like.device)
     if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous int32 tensor of shape ({rows}, {k})")
-    return out
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape ({rows}, {k})")
+    return _on(out, like, name)
+
+
+def _plan_arg(plan, like):
+    """(pointer, bytes) of a plan tensor on like's device, or (None, 0)."""
+    import torch
+
+    if plan is None:
+        return None, 0
+    if plan.dtype != torch.uint8 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous uint8 tensor from plan()")
+    _on(plan, like, "plan")
+    return plan.data_ptr(), plan.numel()
 
 
 def plan_bytes(num_rows: int) -> int:
@@ -123,15 +145,27 @@ def plan(seq_lens, k: int, row_starts=None, out=None, stream=None):
 
     n = int(seq_lens.shape[0])
     _vec_i32(seq_lens, n, "seq_lens")
-    _vec_i32(row_starts, n, "row_starts")
+    _vec_i32(row_starts, n, "row_starts", seq_lens)
     nbytes = plan_bytes(n)
     if out is None:
         out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=seq_lens.device)
+    else:
+        _plan_arg(out, seq_lens)
     st = _lib().dsatopk_plan(_ptr(seq_lens), _ptr(row_starts), n, int(k), _ptr(out), out.numel(),
                              _stream(stream))
     if st != 0:
         raise DsatopkError(st, "dsatopk_plan")
     return out
+
+
+def plan_error(plan, stream=None) -> int:
+    """The plan's error word (synchronizes the stream): 1 if a split row's
+    wait gave up in a transform call since the plan was built, else 0."""
+    err = ctypes.c_int32(0)
+    st = _lib().dsatopk_plan_error(_ptr(plan), plan.numel(), ctypes.byref(err), _stream(stream))
+    if st != 0:
+        raise DsatopkError(st, "dsatopk_plan_error")
+    return int(err.value)
 
 
 def paged(scores, seq_lens, page_table, page_size: int, k: int, row_starts=None, plan=None,
@@ -143,35 +177,40 @@ def paged(scores, seq_lens, page_table, page_size: int, k: int, row_starts=None,
     0; ``out_raw`` (int32 ``[rows, k]``, or True to allocate one) also
     receives the window positions, slot for slot. Returns ``out``, or
     ``(out, out_raw)`` when ``out_raw`` is given."""
+    import torch
+
     scores = _scores(scores)
     rows = int(scores.shape[0])
-    _vec_i32(seq_lens, rows, "seq_lens")
-    _vec_i32(row_starts, rows, "row_starts")
-    _vec_i32(table_rows, rows, "table_rows")
-    _vec_i32(table_starts, rows, "table_starts")
+    _vec_i32(seq_lens, rows, "seq_lens", scores)
+    _vec_i32(row_starts, rows, "row_starts", scores)
+    _vec_i32(table_rows, rows, "table_rows", scores)
+    _vec_i32(table_starts, rows, "table_starts", scores)
     packed = table_rows is not None or table_starts is not None or out_raw is not None
+    if page_table.dtype != torch.int32:
+        raise ValueError("page_table must be int32")
     if page_table.dim() != 2 or page_table.stride(1) != 1:
         raise ValueError("page_table must be [table rows, width] with contiguous columns")
+    _on(page_table, scores, "page_table")
     if table_rows is None and page_table.shape[0] != rows:
         raise ValueError("page_table must have one row per score row without table_rows")
     out = _out(out, rows, int(k), scores)
     if out_raw is True:
-        out_raw = _out(None, rows, int(k), scores)
+        out_raw = _out(None, rows, int(k), scores, "out_raw")
     elif out_raw is not None:
-        out_raw = _out(out_raw, rows, int(k), scores)
+        out_raw = _out(out_raw, rows, int(k), scores, "out_raw")
+    plan_ptr, plan_n = _plan_arg(plan, scores)
     if not packed:
         st = _lib().dsatopk_paged(
             _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
-            page_table.stride(0), int(page_size), rows, int(k), _ptr(plan),
-            0 if plan is None else plan.numel(), _ptr(out), _stream(stream))
+            page_table.stride(0), int(page_size), rows, int(k), plan_ptr, plan_n, _ptr(out),
+            _stream(stream))
         if st != 0:
             raise DsatopkError(st, "dsatopk_paged")
         return out
     st = _lib().dsatopk_paged_packed(
         _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
         page_table.stride(0), int(page_size), _ptr(table_rows), _ptr(table_starts), rows,
-        int(k), _ptr(plan), 0 if plan is None else plan.numel(), _ptr(out), _ptr(out_raw),
-        _stream(stream))
+        int(k), plan_ptr, plan_n, _ptr(out), _ptr(out_raw), _stream(stream))
     if st != 0:
         raise DsatopkError(st, "dsatopk_paged_packed")
     return out if out_raw is None else (out, out_raw)
@@ -182,14 +221,14 @@ def ragged(scores, seq_lens, out_offsets, k: int, row_starts=None, plan=None, ou
     """RAGGED top-k: int32 ``[rows, k]`` of position + out_offsets[row]."""
     scores = _scores(scores)
     rows = int(scores.shape[0])
-    _vec_i32(seq_lens, rows, "seq_lens")
-    _vec_i32(row_starts, rows, "row_starts")
-    _vec_i32(out_offsets, rows, "out_offsets")
+    _vec_i32(seq_lens, rows, "seq_lens", scores)
+    _vec_i32(row_starts, rows, "row_starts", scores)
+    _vec_i32(out_offsets, rows, "out_offsets", scores)
     out = _out(out, rows, int(k), scores)
+    plan_ptr, plan_n = _plan_arg(plan, scores)
     st = _lib().dsatopk_ragged(
         _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(out_offsets),
-        rows, int(k), _ptr(plan), 0 if plan is None else plan.numel(), _ptr(out),
-        _stream(stream))
+        rows, int(k), plan_ptr, plan_n, _ptr(out), _stream(stream))
     if st != 0:
         raise DsatopkError(st, "dsatopk_ragged")
     return out

@@ -9,19 +9,21 @@
 // page_table[b][j / page_size] * page_size + j % page_size (PAGED); slots
 // past min(k, seq_len_b) hold -1. Ties: lower position first.
 //
-// Work decomposition: one 512-thread workgroup per row. By the row's
-// aligned span (seq_len plus the row start's residue mod 4) the workgroup
-// takes one of
-//   - the trivial path (seq_len <= k): writes positions, reads no score;
-//   - a register path: the whole span is loaded once with 16-byte loads
-//     into registers as keys (up to 8192 or 18432 floats), every later
-//     pass runs over registers;
-//   - a streaming path for longer spans: pass 1 builds the level-1
-//     histogram from global memory; pass 2 re-reads the span, writes the
-//     elements above the threshold bin straight to the output stage and
-//     collects the threshold bin's elements in LDS, where the remaining
-//     digits are resolved. If that bin holds more than the LDS candidate
-//     capacity, the remaining digits re-read the span instead.
+// Work decomposition, by the row's aligned span (seq_len plus the row
+// start's residue mod 4) and the batch's score stride (no span exceeds it):
+//   - trivial rows (seq_len <= k) write their positions and read no score;
+//   - register rows (span <= 32768): one workgroup per row loads the whole
+//     span once with 16-byte loads and keeps it in registers as keys; every
+//     later pass runs over registers (1024 threads per row for small
+//     batches of short strides, 256 threads up to a 16384 stride, 512
+//     threads for longer strides);
+//   - long rows of batches with few of them (split rows): cut into
+//     segments of 4096 or 8192 floats, each held in registers by one
+//     workgroup of the register kernel; the segments merge their digit
+//     histograms through an exchange area in the plan buffer;
+//   - the other long rows: streamed once by a 1024-thread workgroup that
+//     keeps the pairs above a running threshold in LDS (a two-pass re-read
+//     serves the rare rows that defeat it).
 // The pages' CUDA design (register rows up to 8192 / 16384, a streaming
 // template, thread-block clusters for very long rows; PR #26788 and
 // PR #36684 digests) is prior art here: the widths and the capacities are
@@ -67,7 +69,21 @@ struct Params {
   const int32_t* table_rows;
   const int32_t* table_starts;
   int32_t* out_raw;
+  // register kernel: its first `workers` workgroups serve split segments
+  // (claimed from the plan), the others one row each
+  int32_t workers;
+  // who reads the long rows that are not split (see LongMode)
+  int32_t long_mode;
 };
+
+// The long rows that are not split: with no plan, the streaming kernel
+// (one workgroup per row of the batch); with a plan of a batch of more than
+// kMaxSplitRows rows, the streaming kernel's persistent grid serves the
+// plan's streamed list and the register kernel, in pieces, any long row the
+// plan does not list (a plan built for other lengths); with a plan of a
+// smaller batch (every long row split), the register kernel, in pieces, any
+// long row the plan does not split.
+enum LongMode : int32_t { kLongPerRow = 0, kLongListed = 1, kLongInPieces = 2 };
 
 // Row classes by aligned span. A row's class is recomputed by every kernel
 // from the current seq_lens / row_starts; the plan only packs the rows of a
@@ -75,58 +91,71 @@ struct Params {
 enum RowClass : int32_t { kClassShort = 0, kClassMid = 1, kClassBig = 2, kClassLong = 3 };
 constexpr int kNumClasses = 4;
 
-// Plan layout (int32 words): header, then the rows of each class
-// (segments in class order), then each row's class at planning time.
-constexpr int kPlanMagic = 0x44534b32;  // "DSK2"
+// Plan layout (int32 words): a 64-word header; the rows of each class
+// (class order); each row's class, segment count and exchange slot; the
+// (row, segment) work items of split rows; one exchange area per split row.
+constexpr int kPlanMagic = 0x44534b33;  // "DSK3"
 constexpr int kPlanHeaderWords = 64;
 enum PlanWord : int32_t {
   kPlanWordMagic = 0,
   kPlanWordRows = 1,
   kPlanWordK = 2,
-  kPlanWordCount = 4,   // [4] rows per class
-  kPlanWordOffset = 8,  // [4] first list index per class
-  kPlanWordSplit = 12,  // long rows cut into segments (each owns an exchange area)
-  kPlanWordItems = 13,  // (row, segment) work items of those rows
-  kPlanWordError = 14,  // set if a segment ever gave up waiting (never, if correct)
+  kPlanWordCount = 4,        // [4] rows per class
+  kPlanWordOffset = 8,       // [4] first list index per class
+  kPlanWordSplit = 12,       // long rows cut into segments (each owns an exchange area)
+  kPlanWordItems = 13,       // (row, segment) work items of those rows
+  kPlanWordError = 14,       // set when a split segment gave up waiting for its row
+  kPlanWordSpin = 15,        // polls before such a wait gives up (0: kSpinLimit)
+  kPlanWordSegLen = 16,      // floats per segment of the split rows
+  kPlanWordStreamed = 17,    // long rows read whole by the streaming kernel (class-list order)
 };
 
-// Long rows are cut into segments of kSegLen aligned floats, one workgroup
-// each, holding its segment in registers like a short row. The segments of
-// a row merge their digit histograms through the row's exchange area in
-// the plan buffer (this replaces the pages' thread-block cluster path:
-// CDNA has no clusters or distributed shared memory).
-constexpr int kSegLen = kSmallVec * 4 * kBlock;                                  // 8192
-constexpr int kMaxSeg = (DSATOPK_MAX_SEQ_LEN + 3 + kSegLen - 1) / kSegLen;         // 17
+// Long rows are cut into segments of 4096 or 8192 aligned floats, one
+// workgroup each, holding its segment in registers like a short row. The
+// segments of a row merge their digit histograms through the row's exchange
+// area in the plan buffer (this replaces the pages' thread-block cluster
+// path: CDNA has no clusters or distributed shared memory). Segments are
+// 8192 floats unless the batch's long rows would then give fewer segments
+// than the chip has CUs.
+constexpr int kSegShort = 4096;
+constexpr int kSegLong = 8192;
+constexpr int kChipCUs = 256;
+constexpr int kMaxSeg = (DSATOPK_MAX_SEQ_LEN + 3 + kSegShort - 1) / kSegShort;  // 33
 // A batch's long rows are split only if there are at most this many (about
-// one per CU): each then gets the whole GPU's help. With more, the GPU is
-// already full with one streaming workgroup per long row, which does less
-// work per element than the split rows' merge rounds.
+// one per CU): each then gets the whole GPU's help. With more, one
+// workgroup per long row already fills the GPU and does less work per
+// element than the split rows' merge rounds.
 constexpr int kMaxSplitRows = 256;
+// Split workers per launch: at most the register kernel's three
+// workgroups per CU, so that the workers, the first workgroups of the grid,
+// are resident together (see SplitSync).
+constexpr int kMaxWorkers = 3 * kChipCUs;
 constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
 
-// Exchange area of one split row (int32 words). Every region is zero at
-// the start of a call; the last segment to finish re-zeroes what the call
-// used.
-constexpr int kCandCapG = 2048;  // threshold-bin elements resolved by one wave
+// Exchange area of one split row (int32 words). The histogram and the
+// counters are zero at the start of a call: the plan zeroes them, every
+// round's last arriver re-zeroes the bins it read, and the row's last
+// segment to finish resets the counters.
+constexpr int kCandCapG = 2048;  // threshold-bin elements resolved by the last segment
+// Each counter has a 128-byte line of its own: the device-scope atomics on
+// one address are serialized (about 12 ns each on MI355X), and the polls of
+// the round word should not queue behind the arrivals.
 enum XWord : int32_t {
-  kXA = 0,              // 4096 bins: key bits 31..20
-  kXCand = 4096,        // kCandCapG (key, position) pairs of the level-1 bin
-  kXB = 8192,           // fallback digits: 4096 bins, key bits 19..8
-  kXC = 12288,          // 256 bins: key bits 7..0
-  kXD = 12544,          // 4096 bins: position bits 16..5
-  kXE = 16640,          // 32 bins: position bits 4..0
-  kXFlag = 16672,       // 64-bit: last published round and its result
-  kXArrive = 16674,     // segments arrived (all rounds)
-  kXNCand = 16675,      // candidate pairs written
-  kXOut = 16676,        // output slots taken
-  kXDone = 16677,       // segments finished
-  kXFallback = 16678,   // the fallback digits were used
-  kXWords = 16704,      // multiple of 64 words (256 bytes)
+  kXHist = 0,       // 4096 bins: the current digit round's merged histogram
+  kXCand = 4096,    // kCandCapG (key, position) pairs of the level-1 bin
+  kXFlag = 8192,    // 64-bit: last published round and its result
+  kXArrive = 8224,  // segments arrived (all rounds)
+  kXNCand = 8256,   // candidate pairs written
+  kXOut = 8288,     // output slots taken
+  kXDone = 8320,    // segments finished
+  kXFail = 8352,    // a segment of the row gave up waiting
+  kXWords = 8384,   // multiple of 64 words (256 bytes)
 };
 
 __host__ __device__ constexpr int64_t plan_split_cap(int64_t rows) {
   return rows < kMaxSplitRows ? rows : kMaxSplitRows;
 }
+__host__ __device__ constexpr int64_t plan_cls_word(int64_t rows) { return kPlanHeaderWords + rows; }
 __host__ __device__ constexpr int64_t plan_nseg_word(int64_t rows) { return kPlanHeaderWords + 2 * rows; }
 __host__ __device__ constexpr int64_t plan_slot_word(int64_t rows) { return kPlanHeaderWords + 3 * rows; }
 __host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
@@ -136,8 +165,8 @@ __host__ __device__ constexpr int64_t plan_xarea_word(int64_t rows) {
 __host__ __device__ constexpr int64_t plan_words(int64_t rows) {
   return plan_xarea_word(rows) + plan_split_cap(rows) * kXWords;
 }
-__host__ __device__ constexpr int32_t segments_for(int32_t span) {
-  return (span + kSegLen - 1) / kSegLen;
+__host__ __device__ constexpr int32_t segments_for(int32_t span, int32_t seg_len) {
+  return (span + seg_len - 1) / seg_len;
 }
 
 // Output of one row: window position j -> emitted value. In PAGED mode the
@@ -239,12 +268,14 @@ struct SmemRegB {
 };
 using SmemReg = SmemRegB<kBlock>;
 
-// The split path also keeps small digit histograms beside its candidate
-// list, which fills the 4096-word array.
-struct SmemSplit : SmemReg {
+// A split segment's workgroup (the register kernel's 512 threads) also
+// keeps an 8-bit digit histogram, the positions of a small tie class and
+// the words of its row's rounds and of its claims.
+template <int BS>
+struct SmemSplitB : SmemRegB<BS> {
   uint32_t h2[256];
-  uint32_t h3[256];
-  uint32_t h4[16];
+  uint32_t tie[64];
+  uint32_t word[8];
 };
 
 // Shared memory of the streaming path.
@@ -293,15 +324,18 @@ constexpr int kS1Cap = 8160;
 // barrier of chunk c + 1). A compaction ranks its kept pairs by per-wave
 // counts in wave_cnt; the warm start, which appends once between barriers,
 // counts in n0. After the last chunk the final cut reads the list in place.
-struct SmemS1 {
-  uint2 cand[kS1Cap];
+template <int BS, int CAP>
+struct SmemListB {
+  static constexpr int kCap = CAP;
+  uint2 cand[CAP];
   uint32_t hist[kBins];                 // digit histograms; finally the output stage
-  uint32_t wave_cnt[kLongBlock / 64];   // per-wave counts (compaction, stage)
+  uint32_t wave_cnt[BS / 64];           // per-wave counts (compaction, stage)
   uint32_t ccnt[4];
   uint32_t n0;
   uint32_t tie_n;
   uint32_t bcast[4];
 };
+using SmemS1 = SmemListB<kLongBlock, kS1Cap>;
 
 // Window of one row, addressed from the 16-byte aligned column at or below
 // row_start: aligned index a holds window position a - rem, and only
@@ -566,9 +600,8 @@ __device__ __forceinline__ BinHit wave0_find(const uint32_t* hist, uint32_t need
 // barrier every wave finds the crossing wave, then lane, then bin by
 // itself. Its second-level reads of the histogram need a closing barrier
 // before anyone may write it again.
-template <int NB, bool kDesc, int BS>
-__device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t need,
-                                                 SmemRegB<BS>& sm) {
+template <int NB, bool kDesc, int BS, class Sm>
+__device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t need, Sm& sm) {
   constexpr int W = BS / 64;
   constexpr int PER = NB / BS;
   static_assert(PER >= 4 && PER % 4 == 0 && PER <= 64 && W <= 64, "one 16-byte read per run step");
@@ -627,11 +660,15 @@ template <int BS>
 struct HasWaveSums<SmemRegB<BS>> {
   static constexpr bool value = BS >= kBlock;
 };
+template <int BS>
+struct HasWaveSums<SmemSplitB<BS>> {
+  static constexpr bool value = BS >= kBlock;
+};
 
 template <int NB, bool kDesc, int BS, class Sm>
 __device__ __forceinline__ BinHit group_find(const uint32_t* hist, uint32_t need, Sm& sm) {
   if constexpr (BS >= kBlock && NB >= 4 * BS && HasWaveSums<Sm>::value)
-    return all_waves_find<NB, kDesc, BS>(hist, need, sm);
+    return all_waves_find<NB, kDesc, BS, Sm>(hist, need, sm);
   else
     return wave0_find<NB, kDesc>(hist, need, sm);
 }
@@ -1092,6 +1129,90 @@ __device__ __forceinline__ bool compact_candidates(SmemS1& sm, uint32_t k, uint3
   return n + (uint32_t)kS1Chunk <= (uint32_t)kS1Cap;
 }
 
+// The exact cut over a row's (key, position) list in LDS (n >= k pairs,
+// every key >= T, every pair the row's top k needs among them), then the
+// stage and the emit of the k selected positions.
+template <bool kPaged, int BS, class Sm>
+__device__ __forceinline__ void list_cut_emit(const RowView& rv, int32_t k, const Emit<kPaged>& em,
+                                              Sm& sm, uint32_t n, uint32_t T) {
+  // The cut and the stage run on the list where it stands (at least k
+  // pairs). On offsets above T when fewer than k pairs reach the offset
+  // bound (those are then all above the cut, where their order does not
+  // matter); on the keys themselves otherwise.
+  const uint32_t kk = (uint32_t)k;
+  // The row's page-table entries, when at most kBins - kMaxK, into registers
+  // now (their loads overlap the cut), and into the histogram's upper part
+  // once the cut is found: the stage below it takes at most kMaxK words.
+  // The emit then looks them up in LDS instead of waiting on global loads.
+  constexpr int kTabCap = kBins - kMaxK;
+  constexpr int kTabPer = kTabCap / BS;
+  static_assert(kTabCap % BS == 0, "whole table entries per thread");
+  const int32_t L = rv.span - rv.rem;
+  const int2 tsp = em.table_span(L);
+  const bool tab = kPaged && tsp.y <= kTabCap;
+  int32_t tv[kTabPer];
+  if (tab) {
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) {
+      const int32_t e = q * BS + tix();
+      tv[q] = e < tsp.y ? em.pt[tsp.x + e] : 0;
+    }
+  }
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  // Level 1 on the offsets first: every offset at the bound lands in the
+  // top bin (with the offsets just below it), so a top bin of fewer than
+  // k pairs means fewer than k at the bound. Otherwise (keys far above T)
+  // the histogram is rebuilt on the keys.
+  const uint32_t one = opaque_one();
+  {
+    const ListSrc<BS> so{sm.cand, n, T, true};
+    so.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
+  }
+  __syncthreads();
+  const bool offsets = __builtin_amdgcn_readfirstlane(sm.hist[kBins - 1]) < kk;
+  const ListSrc<BS> src{sm.cand, n, T, offsets};
+  if (!offsets) {
+    __syncthreads();  // every wave has read the top bin
+    clear_bins<kBins, BS>(sm.hist);
+    __syncthreads();
+    src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
+    __syncthreads();
+  }
+  const Cut cut = refine_in_registers<BS>(src, sm, kk, offsets);
+  // every search of the cut ended with a barrier after its last histogram
+  // read; the tie ranking reads only the first 64 words
+  int32_t* table = stage + kMaxK;
+  Emit<kPaged> et = em;
+  if (tab) {
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) {
+      const int32_t e = q * BS + tix();
+      if (e < tsp.y) table[e] = tv[q];
+    }
+    et.staged = true;
+    et.pt_first = tsp.x;
+  }
+  if (cut.pos == kAllPos) {
+    const uint32_t lo = cut.prefix << cut.shift;
+    const uint32_t thr = lo ? lo : 1u;
+    stage_selected<BS, false>(
+        src, [thr](uint32_t kv, int32_t) { return kv >= thr; }, kk, stage, sm);
+  } else {
+    const uint32_t tau = cut.prefix;
+    const int32_t pos = cut.pos;
+    stage_selected<BS, true>(
+        src,
+        [tau, pos](uint32_t kv, int32_t j) {
+          return (kv != 0u) & ((kv > tau) | ((kv == tau) & (j <= pos)));
+        },
+        kk, stage, sm);
+  }
+  __syncthreads();
+  write_stage<kPaged, BS>(et, stage, L, k, table);
+}
+
 template <bool kPaged, int BS>
 __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const Emit<kPaged>& em,
                                             SmemS1& sm, SmemRegB<BS>& fin, const Prefetch pf) {
@@ -1305,84 +1426,237 @@ __device__ __forceinline__ bool row_stream1(const RowView& rv, int32_t k, const 
     touched = __builtin_amdgcn_raw_buffer_load_b32(r, tix() * 64, 0, 0);
   }
 
-  // The cut and the stage run on the list where it stands (at least k
-  // pairs). On offsets above T when fewer than k pairs reach the offset
-  // bound (those are then all above the cut, where their order does not
-  // matter); on the keys themselves otherwise.
-  const uint32_t kk = (uint32_t)k;
-  // The row's page-table entries, when at most kBins - kMaxK, into registers
-  // now (their loads overlap the cut), and into the histogram's upper part
-  // once the cut is found: the stage below it takes at most kMaxK words.
-  // The emit then looks them up in LDS instead of waiting on global loads.
-  constexpr int kTabCap = kBins - kMaxK;
-  constexpr int kTabPer = kTabCap / BS;
-  static_assert(kTabCap % BS == 0, "whole table entries per thread");
-  const int32_t L = rv.span - rv.rem;
-  const int2 tsp = em.table_span(L);
-  const bool tab = kPaged && tsp.y <= kTabCap;
-  int32_t tv[kTabPer];
-  if (tab) {
+  list_cut_emit<kPaged, BS>(rv, k, em, sm, n, T);
+  asm volatile("" ::"v"(touched));  // keeps the touch (landed long before)
+  return true;
+}
+
+// Long rows in register pieces (the 512-thread register kernel). A long
+// row that is not split is read in pieces of kPiece floats, each held in
+// registers while it is scanned (8 float4 per thread: with more, the
+// pieces' bookkeeping no longer fits the kernel's 80 VGPRs). T opens at the
+// key of rank kt in the first piece, kt the count that, at the piece's
+// rate, puts about 1.25 k keys of the whole span at or above it (kt = k
+// when the span is at most 1.25 pieces); the 24-bit prefix of that key
+// (level-1 and level-2 digits) gives T. Every piece's pairs with key >= T
+// go to an LDS list. When a piece's pairs would overflow the list, T rises
+// to the floor of the offset bin that holds the k-th largest key of the
+// list and the piece together, and the list keeps its pairs >= T. Once the
+// last piece is in and at least k pairs reached T, every key of the row's
+// top k is in the list, and the final cut runs on it. A row where fewer
+// than k keys reached T (its largest keys crowd its first piece), or whose
+// pairs overflow the list at every threshold it can reach (heavy ties), is
+// re-read by the two-pass path.
+constexpr int kPieceVec = 8;
+constexpr int kPiece = kPieceVec * 4 * kBigBlock;  // 16384
+constexpr int kListCap = 4352;
+// The list with the running sums of all-wave searches (the keys of a piece
+// stay in registers through the searches, which a one-wave search of 4096
+// bins would push into spills): three fit a CU's 160 KB of LDS.
+struct SmemPieces : SmemListB<kBigBlock, kListCap> {
+  uint32_t lsum[kBigBlock];
+  uint32_t wsum[kBigBlock / 64];
+};
+template <>
+struct HasWaveSums<SmemPieces> {
+  static constexpr bool value = true;
+};
+
+// How many register elements of the workgroup have key >= thr (every
+// thread gets the total). wave_cnt is free on entry and again on return.
+template <int BS, class Src>
+__device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
+                                                   uint32_t* wave_cnt) {
+  uint32_t mine = 0;  // this wave's count (scalar)
+  src.for_each([&](uint32_t kk, int32_t) {
+    mine += (uint32_t)__builtin_popcountll(__ballot(kk >= thr));
+  });
+  if (lane_id() == 0) wave_cnt[wave_id()] = mine;
+  __syncthreads();
+  uint32_t tot = 0;
 #pragma unroll
-    for (int q = 0; q < kTabPer; ++q) {
-      const int32_t e = q * BS + tix();
-      tv[q] = e < tsp.y ? em.pt[tsp.x + e] : 0;
-    }
+  for (int v = 0; v < BS / 64; ++v) tot += wave_cnt[v];
+  tot = __builtin_amdgcn_readfirstlane(tot);
+  __syncthreads();
+  return tot;
+}
+
+// Appends the register elements with key >= thr to cand[n ..) in register
+// order (slots at or past CAP are dropped: the caller has checked the
+// count) and returns the new length.
+template <int BS, int CAP, class Src>
+__device__ __forceinline__ uint32_t append_at_least(const Src& src, uint32_t thr, uint2* cand,
+                                                    uint32_t n, uint32_t* wave_cnt) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  uint32_t mine = 0;
+  src.for_each([&](uint32_t kk, int32_t) { mine = add_lane_bit(mine, __ballot(kk >= thr)); });
+  const uint32_t incl = wave_inclusive_sum(mine);
+  if (lane == 63) wave_cnt[w] = incl;
+  __syncthreads();
+  const uint32_t c = lane < BS / 64 ? wave_cnt[lane] : 0u;
+  const uint32_t ic = wave_inclusive_sum(c);
+  uint32_t slot = n + incl - mine + (w ? read_lane(ic, w - 1) : 0u);
+  const uint32_t tot = read_lane(ic, BS / 64 - 1);
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = kk >= thr;
+    const uint64_t m = __ballot(s);
+    if (s & (slot < (uint32_t)CAP)) cand[slot] = make_uint2(kk, (uint32_t)j);
+    slot = add_lane_bit(slot, m);
+  });
+  __syncthreads();
+  return n + tot;
+}
+
+// Keeps the list's pairs with key >= Tn, in order, in place, and returns
+// the new length. One pair per thread at a time: each block of BS pairs is
+// read, ranked and written at or below its own start (all of a block's
+// reads come before its writes, and its writes land below the next block).
+template <int BS>
+__device__ __forceinline__ uint32_t compact_inplace(uint2* cand, uint32_t n, uint32_t Tn,
+                                                    uint32_t* wave_cnt) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  uint32_t out = 0;
+  for (uint32_t b0 = 0; b0 < n; b0 += BS) {
+    const uint32_t i = b0 + (uint32_t)tix();
+    const uint2 e = i < n ? cand[i] : make_uint2(0u, 0u);
+    const bool keep = (i < n) & (e.x >= Tn);
+    const uint64_t m = __ballot(keep);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (lane == 0) wave_cnt[w] = (uint32_t)__builtin_popcountll(m);
+    __syncthreads();
+    const uint32_t c = lane < BS / 64 ? wave_cnt[lane] : 0u;
+    const uint32_t ic = wave_inclusive_sum(c);
+    const uint32_t pre = w ? read_lane(ic, w - 1) : 0u;
+    if (keep) cand[out + pre + rank] = e;
+    out += read_lane(ic, BS / 64 - 1);
+    __syncthreads();
   }
+  return out;
+}
+
+// T rises to the floor of the offset bin holding the k-th largest key of
+// the list and of the register keys >= T together (offsets key - T in
+// 12-bit digits, the top bin taking every larger offset; inside a bin of
+// more than 64 pairs the next 12 offset bits), and the list keeps its pairs
+// >= the new T. At least k keys of the two reach it.
+template <int BS, class Src, class Sm>
+__device__ __forceinline__ void raise_threshold(const Src& src, Sm& sm, uint32_t k, uint32_t& T,
+                                                uint32_t& n) {
+  const uint32_t t = (uint32_t)tix();
+  const uint32_t T0 = T;
+  const uint32_t one = opaque_one();
+  auto bin1 = [T0](uint32_t kk) {
+    const uint32_t r = (kk - T0) >> 12;
+    return r < (uint32_t)kBins ? r : (uint32_t)kBins - 1u;
+  };
   clear_bins<kBins, BS>(sm.hist);
   __syncthreads();
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  // Level 1 on the offsets first: every offset at the bound lands in the
-  // top bin (with the offsets just below it), so a top bin of fewer than
-  // k pairs means fewer than k at the bound. Otherwise (keys far above T)
-  // the histogram is rebuilt on the keys.
-  const uint32_t one = opaque_one();
-  {
-    const ListSrc<BS> so{sm.cand, n, T, true};
-    so.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
-  }
+  for (uint32_t i = t; i < n; i += BS) lds_add(&sm.hist[bin1(sm.cand[i].x)], one);
+  src.for_each([&](uint32_t kk, int32_t) {
+    if (kk >= T0) lds_add(&sm.hist[bin1(kk)], one);
+  });
   __syncthreads();
-  const bool offsets = __builtin_amdgcn_readfirstlane(sm.hist[kBins - 1]) < kk;
-  const ListSrc<BS> src{sm.cand, n, T, offsets};
-  if (!offsets) {
-    __syncthreads();  // every wave has read the top bin
+  const BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
+  uint32_t Tn = T0 + (h.bin << 12);
+  if (h.cnt > 64u && h.bin < (uint32_t)kBins - 1u) {
     clear_bins<kBins, BS>(sm.hist);
     __syncthreads();
-    src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
-    __syncthreads();
-  }
-  const Cut cut = refine_in_registers<BS>(src, sm, kk, offsets);
-  // every search of the cut ended with a barrier after its last histogram
-  // read; the tie ranking reads only the first 64 words
-  int32_t* table = stage + kMaxK;
-  Emit<kPaged> et = em;
-  if (tab) {
-#pragma unroll
-    for (int q = 0; q < kTabPer; ++q) {
-      const int32_t e = q * BS + tix();
-      if (e < tsp.y) table[e] = tv[q];
+    const uint32_t hb = h.bin;
+    for (uint32_t i = t; i < n; i += BS) {
+      const uint32_t r = sm.cand[i].x - T0;
+      if ((r >> 12) == hb) lds_add(&sm.hist[r & 0xfffu], one);
     }
-    et.staged = true;
-    et.pt_first = tsp.x;
+    src.for_each([&](uint32_t kk, int32_t) {
+      const uint32_t r = kk - T0;
+      if ((kk >= T0) & ((r >> 12) == hb)) lds_add(&sm.hist[r & 0xfffu], one);
+    });
+    __syncthreads();
+    const BinHit h2 = group_find<kBins, true, BS>(sm.hist, k - h.before, sm);
+    Tn += h2.bin;
   }
-  if (cut.pos == kAllPos) {
-    const uint32_t lo = cut.prefix << cut.shift;
-    const uint32_t thr = lo ? lo : 1u;
-    stage_selected<BS, false>(
-        src, [thr](uint32_t kv, int32_t) { return kv >= thr; }, kk, stage, sm);
-  } else {
-    const uint32_t tau = cut.prefix;
-    const int32_t pos = cut.pos;
-    stage_selected<BS, true>(
-        src,
-        [tau, pos](uint32_t kv, int32_t j) {
-          return (kv != 0u) & ((kv > tau) | ((kv == tau) & (j <= pos)));
-        },
-        kk, stage, sm);
+  n = compact_inplace<BS>(sm.cand, n, Tn, sm.wave_cnt);
+  T = Tn;
+}
+
+// A long row in pieces (span > 2 * kPiece). Returns false, having written
+// nothing, when fewer than k keys reach T or the list cannot hold the
+// pairs at or above any threshold it can reach (the caller then runs the
+// two-pass path).
+template <bool kPaged>
+__device__ __forceinline__ bool row_in_pieces(const RowView& rv, int32_t k, const Emit<kPaged>& em,
+                                              SmemPieces& sm) {
+  constexpr int BS = kBigBlock;
+  constexpr int NV = kPieceVec;
+  const int32_t t = tix();
+  const int32_t nvec = (rv.span + 3) >> 2;
+  const int32_t npiece = (rv.span + kPiece - 1) / kPiece;
+  const uint32_t kk = (uint32_t)k;
+  uint32_t T = 1;
+  uint32_t n = 0;
+  for (int32_t pc = 0; pc < npiece; ++pc) {
+    const int32_t v0 = pc * (kPiece / 4);
+    float4 x[NV];
+    load_vectors<NV, BS>(rv.base4, nvec, v0, x);
+    // register slices 0 .. ilast hold the piece's columns
+    const int32_t rest = (nvec - v0 - 1) / BS;
+    const int32_t ilast = __builtin_amdgcn_readfirstlane(rest < NV - 1 ? rest : NV - 1);
+    // keys, with key 0 for every column outside the window (a branch-free
+    // range test per element: the piece's columns before the window start,
+    // or at or past the span)
+    uint32_t key[NV][4];
+    {
+      const uint32_t lim = (uint32_t)(rv.span - rv.rem);
+      int32_t a = 4 * (v0 + t) - rv.rem;  // window position of element (0, 0)
+      asm volatile("" : "+v"(a));
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t kv = order_key(lane_of(x[i], c));
+          key[i][c] = (uint32_t)(a + i * BS * 4 + c) < lim ? kv : 0u;
+        }
+    }
+    const RegSrc<NV, BS> src{key, v0 * 4 - rv.rem, ilast};
+    if (pc == 0) {
+      clear_bins<kBins, BS>(sm.hist);
+      __syncthreads();
+      {
+        const uint32_t one = opaque_one();
+        src.for_each([&](uint32_t kv, int32_t) { lds_add(&sm.hist[kv >> 20], one); });
+      }
+      __syncthreads();
+      // T: the floor of the 24-bit prefix bin holding the piece's kt-th key
+      const uint32_t kt = (uint32_t)min(
+          k, max(1, (int32_t)((5 * (int64_t)k * kPiece + 4 * rv.span - 1) / (4 * rv.span))));
+      const BinHit h = group_find<kBins, true, BS>(sm.hist, kt, sm);
+      clear_bins<kBins, BS>(sm.hist);
+      __syncthreads();
+      {
+        const uint32_t one = opaque_one();
+        const uint32_t b1 = h.bin;
+        src.for_each([&](uint32_t kv, int32_t) {
+          if ((kv >> 20) == b1) lds_add(&sm.hist[(kv >> 8) & 0xfffu], one);
+        });
+      }
+      __syncthreads();
+      const BinHit h2 = group_find<kBins, true, BS>(sm.hist, kt - h.before, sm);
+      T = (h.bin << 20) | (h2.bin << 8);
+      T = T ? T : 1u;
+      if (h.before + h2.before + h2.cnt > (uint32_t)kListCap) return false;
+    } else if (n + count_at_least<BS>(src, T, sm.wave_cnt) > (uint32_t)kListCap) {
+      raise_threshold<BS>(src, sm, kk, T, n);
+      if (n + count_at_least<BS>(src, T, sm.wave_cnt) > (uint32_t)kListCap) return false;
+    }
+    n = append_at_least<BS, kListCap>(src, T, sm.cand, n, sm.wave_cnt);
   }
-  for (int32_t i = (int32_t)kk + tix(); i < k; i += BS) stage[i] = -1;
-  __syncthreads();
-  write_stage<kPaged, BS>(et, stage, L, k, table);
-  asm volatile("" ::"v"(touched));  // keeps the touch (landed long before)
+  // fewer than k keys of the span reached T (its largest keys crowd its
+  // first piece, or the window holds keys below every threshold, i.e.
+  // all-ones NaNs): the two-pass path
+  if (n < kk) return false;
+  list_cut_emit<kPaged, BS>(rv, k, em, sm, n, T);
   return true;
 }
 
@@ -1446,10 +1720,14 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32
 // (checked on the host), so its row words are in bounds whatever it holds.
 struct RowMeta {
   RowInfo r;
-  int32_t trow;    // PAGED: page-table row
-  int32_t tstart;  // PAGED: table position of window position 0
-  int32_t offset;  // RAGGED: the row's out offset
-  bool split;      // the plan sends the row to the split kernel
+  int32_t trow;     // PAGED: page-table row
+  int32_t tstart;   // PAGED: table position of window position 0
+  int32_t offset;   // RAGGED: the row's out offset
+  int32_t nseg;     // plan: the row's segments (split rows)
+  int32_t slot;     // plan: the row's exchange area (split rows)
+  int32_t seg_len;  // plan: floats per segment
+  bool split;       // the plan sends the row to the split workers
+  bool streamed;    // the plan lists the row as a long row read whole
 };
 
 template <bool kPaged>
@@ -1462,17 +1740,20 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   const bool hp = with_plan && p.plan != nullptr;
   const int32_t* a_pm = hp ? p.plan + kPlanWordMagic : a_len;
   const int32_t* a_pr = hp ? p.plan + kPlanWordRows : a_len;
+  const int32_t* a_pg = hp ? p.plan + kPlanWordSegLen : a_len;
   const int32_t* a_ps = hp ? p.plan + plan_nseg_word(p.num_rows) + b : a_len;
   const int32_t* a_pl = hp ? p.plan + plan_slot_word(p.num_rows) + b : a_len;
+  const int32_t* a_pc = hp ? p.plan + plan_cls_word(p.num_rows) + b : a_len;
   // (readfirstlane: a no-op on scalar loads; a vector load, where the
   // compiler cannot prove the words unchanged, still ends in an SGPR)
   auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(*a); };
   int32_t len = rd(a_len), rs = rd(a_rs), tr = rd(a_tr), ts = rd(a_ts), of = rd(a_of);
-  int32_t pm = rd(a_pm), pr = rd(a_pr), ps = rd(a_ps), pl = rd(a_pl);
+  int32_t pm = rd(a_pm), pr = rd(a_pr), pg = rd(a_pg), ps = rd(a_ps), pl = rd(a_pl),
+          pc = rd(a_pc);
   // every value is needed here: the compiler may not sink a load into the
   // branch that uses it (which would put it behind another load's wait)
   asm volatile("" : "+s"(len), "+s"(rs), "+s"(tr), "+s"(ts), "+s"(of), "+s"(pm), "+s"(pr),
-               "+s"(ps), "+s"(pl));
+               "+s"(pg), "+s"(ps), "+s"(pl), "+s"(pc));
   RowMeta m;
   RowInfo& r = m.r;
   r = classify(len, p.row_starts ? rs : 0, p.k);
@@ -1483,8 +1764,13 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   m.trow = __builtin_amdgcn_readfirstlane((kPaged && p.table_rows) ? tr : (int32_t)b);
   m.tstart = __builtin_amdgcn_readfirstlane((kPaged && p.table_starts) ? ts : 0);
   m.offset = __builtin_amdgcn_readfirstlane(kPaged ? 0 : of);
-  m.split = hp && pm == kPlanMagic && pr == p.num_rows && r.cls == kClassLong && ps >= 2 &&
-            ps == segments_for(r.span) && pl >= 0 && pl < plan_split_cap(p.num_rows);
+  m.nseg = ps;
+  m.slot = pl;
+  m.seg_len = pg;
+  const bool ours = hp && pm == kPlanMagic && pr == p.num_rows;
+  m.split = ours && r.cls == kClassLong && (pg == kSegShort || pg == kSegLong) && ps >= 2 &&
+            ps == segments_for(r.span, pg) && pl >= 0 && pl < plan_split_cap(p.num_rows);
+  m.streamed = ours && pc == kClassLong && ps == 0;
   return m;
 }
 
@@ -1608,73 +1894,9 @@ __global__ __launch_bounds__(kBlock) void rows_mid_kernel(const Params p) {
     row_in_registers<kLargeVec>(rv, p.k, em, sm);
 }
 
-// Every row up to 32768 floats of a batch with a score stride above 16384
-// floats, in one launch (a launch for a class with no rows in the batch
-// still costs several microseconds): 512 threads per row, holding 4, 8 or
-// 16 float4 each by the row's span. At 80 VGPRs three rows share a CU, so
-// one row's searches overlap the others' loads (for spans above 16384, two
-// rows of 1024 threads with 8 float4 each ran 10-50% slower).
-template <bool kPaged>
-__global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) void
-rows_reg_kernel(const Params p) {
-  const int64_t b = blockIdx.x;
-  const RowMeta m = row_meta<kPaged>(p, b, false);
-  const RowInfo& r = m.r;
-  if (r.cls == kClassLong) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
-  if (r.L <= p.k) {
-    write_trivial<kPaged, kBigBlock>(em, r.L, p.k);
-    return;
-  }
-  __shared__ SmemRegB<kBigBlock> sm;
-  const RowView rv = row_view(p, b, r);
-  if (r.span <= kBigVec * kBigBlock)
-    row_in_registers<kBigVec / 4, kPaged, kBigBlock>(rv, p.k, em, sm);
-  else if (r.span <= kBigVec * 2 * kBigBlock)
-    row_in_registers<kBigVec / 2, kPaged, kBigBlock>(rv, p.k, em, sm);
-  else
-    row_in_registers<kBigVec, kPaged, kBigBlock>(rv, p.k, em, sm);
-}
-
-// Whether row b is served by the split kernel: it was planned as a split
-// row and still has the planned number of segments.
-__device__ __forceinline__ bool split_served(const Params& p, int64_t b, const RowInfo& r) {
-  if (!plan_ok(p) || r.cls != kClassLong) return false;
-  const int32_t S = p.plan[plan_nseg_word(p.num_rows) + b];
-  const int32_t slot = p.plan[plan_slot_word(p.num_rows) + b];
-  return S >= 2 && S == segments_for(r.span) && slot >= 0 && slot < plan_split_cap(p.num_rows);
-}
-
-// Longer spans, streamed, one 1024-thread workgroup per row: the long rows
-// the split kernel does not serve.
-template <bool kPaged>
-__global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
-rows_long_kernel(const Params p) {
-  const int64_t b = blockIdx.x;
-  const RowMeta m = row_meta<kPaged>(p, b, true);
-  const RowInfo& r = m.r;
-  if (r.cls != kClassLong || m.split) return;
-  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
-  if (r.L <= p.k) {
-    write_trivial<kPaged, kLongBlock>(em, r.L, p.k);
-    return;
-  }
-  __shared__ union {
-    SmemS1 one;
-    SmemRegB<kLongBlock> fin;
-    SmemStream two;
-  } sm;
-  const RowView rv = row_view(p, b, r);
-  const Prefetch pf = next_row(p, b, kPrefetchAhead, kClassLong, kS1Depth * kS1Chunk);
-  if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
-    __syncthreads();
-    row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
-  }
-}
-
 // A published round result: round number in bits 63..56, the payload in
 // the low 56 bits (a bin search: bin << 36 | before << 18 | count, each
-// count < 2^18; a resolved cut: pos << 32 | tau, pos = 0x3ffff for "all").
+// count < 2^18).
 __device__ __forceinline__ uint64_t pack_round(uint32_t round, uint64_t payload) {
   return ((uint64_t)round << 56) | payload;
 }
@@ -1688,104 +1910,124 @@ __device__ __forceinline__ BinHit unpack_hit(uint64_t w) {
   h.cnt = (uint32_t)w & 0x3ffffu;
   return h;
 }
-constexpr uint32_t kPackAllPos = 0x3ffffu;
 
 // Split-row synchronisation. Every access to a row's exchange area is a
 // device-scope atomic (read-modify-write, load or store), and device-scope
 // atomics are coherent across the chip's XCDs; none of them needs the L2
 // write-back or invalidation that release / acquire fences would add at
 // every round. Ordering comes from waiting: before a segment arrives, each
-// of its waves waits until its own atomics have completed, so whoever sees
-// the arrival count complete also sees every contribution. Every segment
-// arrives once per round; the last to arrive computes the round's result
-// and publishes it in one 64-bit word, which the others poll. Polls are
-// bounded: a segment that gives up sets the plan's error word and goes on
-// with whatever it read, so no wave can hang.
+// of its waves waits until its own accesses have completed, so whoever
+// sees the arrival count complete also sees every contribution. Every
+// segment arrives once per round; the last to arrive computes the round's
+// result and publishes it in one 64-bit word, which the others poll.
+// Polls are bounded: a segment that gives up marks its row and the plan as
+// failed and takes no further part in the row (the row's outputs become
+// -1, see split_finish), so no wave can hang.
 //
-// Forward progress: the segments of a row are consecutive work items, i.e.
-// consecutive workgroups; workgroups are dispatched in order, and a row
-// has at most kMaxSeg of them, far fewer than the workgroups that fit on
-// the chip, so the missing segments of a waiting row are always
-// dispatchable.
+// Forward progress: the W split workers are the first W <= 768 workgroups
+// of the register kernel's grid (three fit a CU), worker w serving work
+// items w, w + W, ... in order, and a row's segments are consecutive items.
+// When the workers are resident together, every row completes: a row's
+// segments are served in the same pass over the items, or a row that
+// straddles two passes waits for workers that finish rows of the earlier
+// pass first. Workgroups are dispatched in grid order on an otherwise idle
+// GPU, which makes the workers resident together; HIP does not promise
+// that, and where it does not hold the bounded waits give up instead of
+// hanging, and the plan's error word and the row's -1 outputs report it.
+// (A counter that workers claim items from would not need the promise, but
+// each claim is a device-scope atomic on one address, and hundreds of them
+// serialize for tens of microseconds.)
 struct SplitSync {
-  uint32_t* x;
-  int32_t S;
-  int32_t* err;
-  uint32_t* s_word;  // LDS: 2 words
+  uint32_t* x;       // the row's exchange area
+  int32_t S;         // segments of the row
+  int32_t* err;      // the plan's error word
+  uint32_t spin;     // polls before a wait gives up
+  uint32_t* word;    // LDS: [0] arrival, [1] [2] round result, [3] gave up
 
   // Returns true in the last segment to arrive at `round` (whole workgroup).
   __device__ __forceinline__ bool arrive(uint32_t round) const {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's atomics completed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's accesses completed
     __syncthreads();
     if (tix() == 0) {
       const uint32_t prev =
           __hip_atomic_fetch_add(&x[kXArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_word[0] = prev == (uint32_t)S * round - 1u;
+      word[0] = prev == (uint32_t)S * round - 1u;
     }
     __syncthreads();
-    return s_word[0] != 0u;
+    return __builtin_amdgcn_readfirstlane(word[0]) != 0u;
   }
 
-  // Last arriver: make `payload` the result of `round`.
+  // Last arriver, whole workgroup: once every thread's exchange accesses
+  // have completed, make `payload` the result of `round`.
   __device__ __forceinline__ void publish(uint32_t round, uint64_t payload) const {
-    if (tix() == 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tix() == 0)
       __hip_atomic_store(reinterpret_cast<uint64_t*>(x + kXFlag), pack_round(round, payload),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 
-  // Everyone: the published result of `round` (the last arriver passes
-  // `mine`, which it just published).
-  __device__ __forceinline__ uint64_t result(uint32_t round, bool last, uint64_t mine) const {
+  // Everyone: the published result of `round` into res (the last arriver
+  // passes `mine`, which it just published). False when the wait gave up.
+  __device__ __forceinline__ bool result(uint32_t round, bool last, uint64_t mine,
+                                         uint64_t& res) const {
     if (tix() == 0) {
       uint64_t w = mine;
+      uint32_t gave_up = 0u;
       if (!last) {
         const uint64_t* f = reinterpret_cast<const uint64_t*>(x + kXFlag);
         uint32_t n = 0;
         while (((w = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 56) <
                round) {
-          if (++n > kSpinLimit) {
+          if (++n > spin) {
+            gave_up = 1u;
+            __hip_atomic_store(&x[kXFail], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
           __builtin_amdgcn_s_sleep(2);
         }
       }
-      s_word[0] = (uint32_t)w;
-      s_word[1] = (uint32_t)(w >> 32);
+      word[1] = (uint32_t)w;
+      word[2] = (uint32_t)(w >> 32);
+      word[3] = gave_up;
     }
     __syncthreads();
-    const uint64_t w = ((uint64_t)s_word[1] << 32) | s_word[0];
-    __syncthreads();  // s_word may be reused right away
-    return w & ((1ull << 56) - 1ull);
+    res = (((uint64_t)word[2] << 32) | word[1]) & ((1ull << 56) - 1ull);
+    return __builtin_amdgcn_readfirstlane(word[3]) == 0u;
   }
 };
 
 // One histogram round: every segment adds its local LDS histogram (NB
 // bins) into the row's global one; the last to arrive gathers the totals
-// into its LDS (one coalesced read) and finds the bin where the running
-// count reaches `need`.
-template <int NB, bool kDesc>
-__device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
-                                                  uint32_t round, uint32_t need,
-                                                  const SplitSync& sy) {
+// into its LDS (one coalesced read), finds the bin where the running count
+// reaches `need`, zeroes the global bins it found set (the next round reuses
+// them) and publishes. False when the wait gave up.
+template <int NB, bool kDesc, int BS>
+__device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
+                                                uint32_t round, uint32_t need,
+                                                const SplitSync& sy, BinHit& hit) {
   const int32_t t = tix();
   __syncthreads();  // local histogram complete
-  for (int32_t i = t; i < NB; i += kBlock) {
+  for (int32_t i = t; i < NB; i += BS) {
     const uint32_t v = lds_hist[i];
     if (v) __hip_atomic_fetch_add(&g_hist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const bool last = sy.arrive(round);
   uint64_t mine = 0;
   if (last) {
-    for (int32_t i = t; i < NB; i += kBlock)
+    for (int32_t i = t; i < NB; i += BS)
       lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     mine = pack_hit(wave_find<NB, kDesc>(lds_hist, need));
+    for (int32_t i = t; i < NB; i += BS)
+      if (lds_hist[i]) __hip_atomic_store(&g_hist[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sy.publish(round, mine);
   }
-  return unpack_hit(sy.result(round, last, mine));
+  uint64_t res;
+  const bool ok = sy.result(round, last, mine, res);
+  hit = unpack_hit(res);
+  return ok;
 }
 
 // The exact cut among n (key, position) pairs in LDS, all inside one
@@ -1795,14 +2037,14 @@ __device__ __forceinline__ BinHit histogram_round(uint32_t* lds_hist, uint32_t* 
 // histogram of the candidates still matching the digits fixed so far.
 // Ties at the k-th key take the lowest positions: a tie class of at most 64
 // elements is gathered and ranked on lane masks, a larger one takes
-// position digits (8, 8 and 1 bits). Returns (tau, pos) packed as the
-// round result: select key > tau, or key == tau + 1 and position <= pos
-// (pos = kPackAllPos: every such key).
-__device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint32_t n,
-                                                        uint32_t need, SmemSplit& sm) {
+// position digits (8, 8 and 1 bits). The result selects key > tau, or
+// key == tau at position <= pos (pos == kAllPos: every such key).
+template <int BS>
+__device__ __forceinline__ Cut resolve_pairs_group(const uint2* cand, uint32_t n, uint32_t need,
+                                                   SmemSplitB<BS>& sm) {
   const int32_t t = tix();
   uint32_t a = 0xffffffffu, o = 0u;
-  for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+  for (uint32_t i = (uint32_t)t; i < n; i += BS) {
     const uint32_t kk = cand[i].x;
     a &= kk;
     o |= kk;
@@ -1834,9 +2076,9 @@ __device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint3
       const int width = top - lo_bit + 1 < 8 ? top - lo_bit + 1 : 8;
       const int sh = top - width + 1;
       const uint32_t above = top == 31 ? 0u : fixed >> (top + 1);
-      sm.h2[t] = 0u;
+      if (t < 256) sm.h2[t] = 0u;
       __syncthreads();
-      for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+      for (uint32_t i = (uint32_t)t; i < n; i += BS) {
         const uint32_t kk = cand[i].x;
         if (top == 31 || (kk >> (top + 1)) == above)
           lds_inc(&sm.h2[(kk >> sh) & ((1u << width) - 1u)]);
@@ -1846,28 +2088,24 @@ __device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint3
       need -= b.before;
       fixed |= b.bin << sh;
       cnt = b.cnt;
-      if (b.cnt == need) {
-        // every key of this digit bin is taken: the cut is its lowest key
-        // (key >= lo; lo = 0 leaves out only the columns outside the window)
-        const uint32_t lo = (fixed >> sh) << sh;
-        return ((uint64_t)kPackAllPos << 32) | (lo ? lo - 1u : 0u);
-      }
+      // every key of this digit bin is taken: the cut is its lowest key
+      if (b.cnt == need) return Cut{0, (fixed >> sh) << sh, kAllPos};
     }
   } else if (cnt == need) {
-    return ((uint64_t)kPackAllPos << 32) | (fixed ? fixed - 1u : 0u);
+    return Cut{0, fixed, kAllPos};
   }
   const uint32_t tau = fixed;  // every key bit decided: the tied key
   if (cnt <= 64u) {
-    for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+    for (uint32_t i = (uint32_t)t; i < n; i += BS) {
       const uint2 e = cand[i];
       if (e.x == tau) {
         const uint32_t slot = atomicAdd(&sm.tie_n, 1u);
-        if (slot < 64u) sm.h3[slot] = e.y;
+        if (slot < 64u) sm.tie[slot] = e.y;
       }
     }
     __syncthreads();
     const int lane = lane_id();
-    const uint32_t p = lane < (int)cnt ? sm.h3[lane] : 0u;
+    const uint32_t p = lane < (int)cnt ? sm.tie[lane] : 0u;
     uint64_t live = cnt >= 64u ? ~0ull : (1ull << cnt) - 1ull;
 #pragma unroll
     for (int b = 16; b >= 0; --b) {
@@ -1881,8 +2119,8 @@ __device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint3
       }
     }
     const uint32_t pos = read_lane(p, live ? __builtin_ctzll(live) : 0);
-    __syncthreads();  // h3 and tie_n may be reused by the caller
-    return ((uint64_t)pos << 32) | (tau - 1u);
+    __syncthreads();  // tie and tie_n may be reused by the caller
+    return Cut{0, tau, (int32_t)pos};
   }
   // a large tie class: position digits 16..9, 8..1, 0
   uint32_t pprefix = 0;
@@ -1891,9 +2129,9 @@ __device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint3
   for (int d = 0; d < 3; ++d) {
     const int sh = pos_shift[d];
     const int wd = pos_width[d];
-    sm.h2[t] = 0u;
+    if (t < 256) sm.h2[t] = 0u;
     __syncthreads();
-    for (uint32_t i = (uint32_t)t; i < n; i += kBlock) {
+    for (uint32_t i = (uint32_t)t; i < n; i += BS) {
       const uint2 e = cand[i];
       if ((e.x == tau) & ((e.y >> (sh + wd)) == pprefix))
         lds_inc(&sm.h2[(e.y >> sh) & ((1u << wd) - 1u)]);
@@ -1903,257 +2141,428 @@ __device__ __forceinline__ uint64_t resolve_pairs_group(const uint2* cand, uint3
     need -= b.before;
     pprefix = (pprefix << wd) | b.bin;
   }
-  return ((uint64_t)pprefix << 32) | (tau - 1u);
+  return Cut{0, tau, (int32_t)pprefix};
 }
 
-// One segment of a split row: the segment sits in registers like a short
-// row; the level-1 histogram is merged over the row in one round; the
-// level-1 bin's elements of the whole row (at most kCandCapG) then go to
-// the row's candidate buffer, and the last segment to arrive resolves the
-// exact cut from them (second round). A level-1 bin too large for the
-// buffer falls back to one round per further digit (12 and 8 key bits, 12
-// and 5 position bits). Output slots come from the row's shared counter.
-template <bool kPaged>
-__device__ __forceinline__ void segment_in_registers(const Params& p, int64_t b, const RowInfo& r,
-                                                     int32_t seg, int32_t S, uint32_t* x,
-                                                     SmemSplit& sm, uint32_t* s_word) {
-  constexpr int NV = kSmallVec;
+// The register elements that `sel` takes, to the row's output at slots
+// taken from the row's output counter (one atomic per call): staged in LDS
+// in register order, then mapped and stored in one coalesced pass. The
+// histogram space must be free.
+template <bool kPaged, int BS, class Src, class Sel>
+__device__ __forceinline__ void split_emit(const Src& src, Sel sel, const Emit<kPaged>& em,
+                                           int32_t L, uint32_t k, uint32_t* x,
+                                           SmemSplitB<BS>& sm) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int32_t t = tix();
+  uint32_t mine = 0;
+  src.for_each([&](uint32_t kk, int32_t j) { mine = add_lane_bit(mine, __ballot(sel(kk, j))); });
+  const uint32_t incl = wave_inclusive_sum(mine);
+  if (lane == 63) sm.wave_cnt[w] = incl;
+  __syncthreads();
+  const uint32_t c = lane < BS / 64 ? sm.wave_cnt[lane] : 0u;
+  const uint32_t ic = wave_inclusive_sum(c);
+  uint32_t slot = incl - mine + (w ? read_lane(ic, w - 1) : 0u);
+  const uint32_t total = read_lane(ic, BS / 64 - 1);
+  if (t == 0)
+    sm.word[5] = total ? __hip_atomic_fetch_add(&x[kXOut], total, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = sel(kk, j);
+    const uint64_t m = __ballot(s);
+    if (s & (slot < (uint32_t)kMaxK)) stage[slot] = j;
+    slot = add_lane_bit(slot, m);
+  });
+  __syncthreads();
+  const uint32_t base = __builtin_amdgcn_readfirstlane(sm.word[5]);
+  auto put = [&](auto value) {
+    for (uint32_t i = (uint32_t)t; i < total; i += BS) {
+      const int32_t j = stage[i];
+      if (((uint32_t)j < (uint32_t)L) & (base + i < k)) em.put((int32_t)(base + i), j, value(j));
+    }
+  };
+  if (kPaged && em.staged)
+    put([&](int32_t j) { return em.value_lds(j, sm.pt); });
+  else
+    put([&](int32_t j) { return em.value(j); });
+  __syncthreads();  // the stage and wave_cnt are free again
+}
+
+// -1 in every output slot of the row (a row whose segments gave up).
+template <bool kPaged, int BS>
+__device__ __forceinline__ void split_fail_row(const Emit<kPaged>& em, uint32_t k) {
+  for (uint32_t i = (uint32_t)tix(); i < k; i += BS) em.put((int32_t)i, -1, -1);
+}
+
+// The end of a segment: it counts itself done once its stores have
+// completed; the row's last segment to finish resets the counters (and,
+// when a segment of the row gave up, writes -1 over the whole row, after
+// every other segment's stores, and clears the histogram). A segment that
+// gave up writes -1 over the row itself too: if a segment of its row never
+// runs, no last segment comes.
+template <bool kPaged, int BS>
+__device__ __forceinline__ void split_finish(const Emit<kPaged>& em, uint32_t k, uint32_t* x,
+                                             int32_t S, bool gave_up, SmemSplitB<BS>& sm) {
+  const int32_t t = tix();
+  if (gave_up) split_fail_row<kPaged, BS>(em, k);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t d =
+        __hip_atomic_fetch_add(&x[kXDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.word[0] = d == (uint32_t)S - 1u;
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sm.word[0]) == 0u) return;
+  const bool failed =
+      __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&x[kXFail], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0u;
+  if (failed) {
+    split_fail_row<kPaged, BS>(em, k);
+    for (int32_t i = t; i < kXCand; i += BS)
+      __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int32_t i = kXFlag + t; i < kXWords; i += BS)
+    __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One segment of a split row (SEG = NV * 4 * 512 floats) in the register
+// kernel. The segment sits in registers like a short row. Round 1 merges
+// the level-1 histogram over the row; every segment then emits its keys
+// above the threshold bin at once (winners). When the bin's elements of the
+// whole row fit the candidate buffer (kCandCapG), each segment writes its
+// own there, arrives and leaves, and the last to arrive resolves the exact
+// cut among them and emits the winners of the bin: no segment waits after
+// round 1. A larger bin takes one more merged round per further digit (12
+// and 8 key bits, 12 and 5 position bits), after which each segment emits
+// its winners of the bin. Output slots come from the row's shared counter.
+template <bool kPaged, int NV>
+__device__ __forceinline__ void split_segment(const Params& p, int64_t b, const RowMeta& m,
+                                              int32_t seg, uint32_t* x, uint32_t spin,
+                                              SmemSplitB<kBigBlock>& sm) {
+  constexpr int BS = kBigBlock;
+  constexpr int SEG = NV * 4 * BS;
+  const RowInfo& r = m.r;
   const int32_t t = tix();
   const int lane = lane_id();
   const int w = wave_id();
   const uint32_t k = (uint32_t)p.k;
-  const SplitSync sy{x, S, p.plan + kPlanWordError, s_word};
+  const int32_t S = m.nseg;
+  const SplitSync sy{x, S, p.plan + kPlanWordError, spin, sm.word};
   const int32_t rem = r.s & 3;
   const float4* base4 = reinterpret_cast<const float4*>(p.scores + b * p.stride + (r.s - rem));
   const int32_t nvec = (r.span + 3) >> 2;
-  const int32_t v0 = seg * (kSegLen / 4);  // first aligned vector of the segment
-  Emit<kPaged> em = row_emit<kPaged>(p, b);
+  const int32_t v0 = seg * (SEG / 4);  // first aligned vector of the segment
+  Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   uint32_t key[NV][4];
   {
     float4 xv[NV];
-    load_vectors<NV, kBlock>(base4, nvec, v0, xv);
+    load_vectors<NV, BS>(base4, nvec, v0, xv);
     const int32_t j0 = v0 * 4 - rem;
-    const int32_t j1 = j0 + kSegLen < r.L ? j0 + kSegLen : r.L;
+    const int32_t j1 = j0 + SEG < r.L ? j0 + SEG : r.L;
     em.stage_table_range(sm.pt, j0, j1);
-    clear_bins<kBins>(sm.hist);
+    clear_bins<kBins, BS>(sm.hist);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int32_t v = v0 + i * kBlock + t;
+      const int32_t v = v0 + i * BS + t;
 #pragma unroll
       for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(xv[i], c));
       if ((v == 0) | (v * 4 + 4 > r.span)) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int32_t a = v * 4 + c;
-          if ((a < rem) | (a >= r.span)) key[i][c] = 0;
+          if ((a < rem) | (a >= r.span)) key[i][c] = 0u;
         }
       }
     }
   }
-  const RegSrc<NV> src{key, v0 * 4 - rem, NV - 1};
+  const RegSrc<NV, BS> src{key, v0 * 4 - rem, NV - 1};
   __syncthreads();
+  {
+    const uint32_t one = opaque_one();
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (v0 + i * kBlock + t < nvec) {
+    for (int i = 0; i < NV; ++i) {
+      if (v0 + i * BS + t < nvec) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) lds_inc(&sm.hist[key[i][c] >> 20]);
+        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
+      }
     }
   }
   uint32_t round = 1;
-  BinHit h = histogram_round<kBins, true>(sm.hist, x + kXA, round++, k, sy);
-  uint32_t need = k - h.before;
-  Cut cut{20, h.bin, kAllPos};
-  if (h.cnt != need && h.cnt <= (uint32_t)kCandCapG) {
-    // Round 2: the level-1 bin's elements of the whole row.
-    const uint32_t lo = h.bin << 20;
-    uint32_t mine = 0;
-    src.for_each([&](uint32_t kk, int32_t) { mine += ((kk - lo) < (1u << 20)) ? 1u : 0u; });
-    const uint32_t incl = wave_inclusive_sum(mine);
-    if (lane == 63) sm.wave_cnt[w] = incl;
-    __syncthreads();
-    uint32_t pre = incl - mine;
-    uint32_t tot = 0;
-    for (int v = 0; v < kWaves; ++v) {
-      pre += v < w ? sm.wave_cnt[v] : 0u;
-      tot += sm.wave_cnt[v];
-    }
-    if (t == 0)
-      s_word[0] = __hip_atomic_fetch_add(&x[kXNCand], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    uint32_t at = s_word[0] + pre;
-    __syncthreads();
-    uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
-    src.for_each([&](uint32_t kk, int32_t j) {
-      if ((kk - lo) < (1u << 20)) {
-        if (at < (uint32_t)kCandCapG)
-          __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        ++at;
-      }
-    });
-    const bool last = sy.arrive(round);
-    uint64_t res = 0;
-    if (last) {
-      uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // 2048 pairs fit 4096 words
-      for (uint32_t i = t; i < h.cnt; i += kBlock) {
-        const uint64_t e = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
-      }
+  BinHit h;
+  bool ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, k, sy, h);
+  if (ok) {
+    uint32_t need = k - h.before;
+    const uint32_t T = h.bin;
+    const bool whole = h.cnt == need;
+    // the winners above the threshold bin (with it, when it is taken whole)
+    split_emit<kPaged, BS>(
+        src,
+        [T, whole](uint32_t kk, int32_t) {
+          const uint32_t d = kk >> 20;
+          return (kk != 0u) & ((d > T) | (whole & (d == T)));
+        },
+        em, r.L, k, x, sm);
+    if (!whole && h.cnt <= (uint32_t)kCandCapG) {
+      // the bin's elements to the row's candidate buffer
+      uint32_t mine = 0;
+      src.for_each([&](uint32_t kk, int32_t) { mine += ((kk != 0u) & ((kk >> 20) == T)) ? 1u : 0u; });
+      const uint32_t incl = wave_inclusive_sum(mine);
+      if (lane == 63) sm.wave_cnt[w] = incl;
       __syncthreads();
-      res = resolve_pairs_group(lcand, h.cnt, need, sm);
-      sy.publish(round, res);
-    }
-    res = sy.result(round, last, res);
-    ++round;
-    const uint32_t tau1 = (uint32_t)res;  // select key > tau1 (or == tau1 + 1 up to pos)
-    const uint32_t pos = (uint32_t)(res >> 32) & kPackAllPos;
-    if (pos == kPackAllPos) {
-      cut = Cut{0, tau1 + 1u, kAllPos};  // key >= tau1 + 1
-    } else {
-      cut = Cut{0, tau1 + 1u, (int32_t)pos};
-    }
-  } else if (h.cnt != need) {
-    // Fallback: one round per further digit.
-    if (t == 0)
-      __hip_atomic_store(&x[kXFallback], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    clear_bins<kBins>(sm.hist);
-    __syncthreads();
-    {
-      const uint32_t pre = cut.prefix;
-      src.for_each([&](uint32_t kk, int32_t) {
-        if ((kk >> 20) == pre) lds_inc(&sm.hist[(kk >> 8) & 0xfffu]);
+      const uint32_t c = lane < BS / 64 ? sm.wave_cnt[lane] : 0u;
+      const uint32_t ic = wave_inclusive_sum(c);
+      const uint32_t pre = incl - mine + (w ? read_lane(ic, w - 1) : 0u);
+      const uint32_t tot = read_lane(ic, BS / 64 - 1);
+      if (t == 0)
+        sm.word[5] = tot ? __hip_atomic_fetch_add(&x[kXNCand], tot, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                         : 0u;
+      __syncthreads();
+      uint32_t at = __builtin_amdgcn_readfirstlane(sm.word[5]) + pre;
+      uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
+      src.for_each([&](uint32_t kk, int32_t j) {
+        if ((kk != 0u) & ((kk >> 20) == T)) {
+          if (at < (uint32_t)kCandCapG)
+            __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          ++at;
+        }
       });
-    }
-    h = histogram_round<kBins, true>(sm.hist, x + kXB, round++, need, sy);
-    need -= h.before;
-    cut = Cut{8, (cut.prefix << 12) | h.bin, kAllPos};
-    if (h.cnt != need) {
-      sm.h2[t] = 0;
+      if (sy.arrive(round++)) {
+        // the last segment: every candidate is in; resolve and emit them
+        const uint32_t n = h.cnt;
+        uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // kCandCapG pairs fill the histogram
+        for (uint32_t i = (uint32_t)t; i < n; i += BS) {
+          const uint64_t e = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+        }
+        if (t == 0) {
+          sm.word[5] =
+              __hip_atomic_fetch_add(&x[kXOut], need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.word[6] = 0u;
+        }
+        __syncthreads();
+        const Cut cut = resolve_pairs_group<BS>(lcand, n, need, sm);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(sm.word[5]);
+        auto put = [&](auto value) {
+          for (uint32_t i0 = 0; i0 < n; i0 += BS) {
+            const uint32_t i = i0 + (uint32_t)t;
+            const uint2 e = i < n ? lcand[i] : make_uint2(0u, 0u);
+            const bool s = (i < n) && is_selected(cut, e.x, (int32_t)e.y);
+            const uint64_t mm = __ballot(s);
+            if (mm == 0) continue;
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+            const int leader = __builtin_ctzll(mm);
+            uint32_t wb = 0;
+            if (lane == leader) wb = atomicAdd(&sm.word[6], (uint32_t)__builtin_popcountll(mm));
+            wb = read_lane(wb, leader);
+            const uint32_t slot = wb + rank;
+            const int32_t j = (int32_t)e.y;
+            if (s & (slot < need) & ((uint32_t)j < (uint32_t)r.L) & (base + slot < k))
+              em.put((int32_t)(base + slot), j, value(j));
+          }
+        };
+        // (candidates come from every segment: the LDS table holds only
+        // this segment's entries)
+        put([&](int32_t j) { return em.value(j); });
+      }
+    } else if (!whole) {
+      // The bin is too large for the buffer: one merged round per digit.
+      clear_bins<kBins, BS>(sm.hist);
       __syncthreads();
       {
-        const uint32_t pre = cut.prefix;
         src.for_each([&](uint32_t kk, int32_t) {
-          if ((kk >> 8) == pre) lds_inc(&sm.h2[kk & 0xffu]);
+          if ((kk != 0u) & ((kk >> 20) == T)) lds_inc(&sm.hist[(kk >> 8) & 0xfffu]);
         });
       }
-      h = histogram_round<256, true>(sm.h2, x + kXC, round++, need, sy);
+      ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, need, sy, h);
+      Cut cut{8, (T << 12) | h.bin, kAllPos};
       need -= h.before;
-      cut = Cut{0, (cut.prefix << 8) | h.bin, kAllPos};
-      if (h.cnt != need) {
-        const uint32_t tau = cut.prefix;
-        clear_bins<kBins>(sm.hist);
+      if (ok && h.cnt != need) {
+        if (t < 256) sm.h2[t] = 0u;
         __syncthreads();
-        src.for_each([&](uint32_t kk, int32_t j) {
-          if (kk == tau) lds_inc(&sm.hist[(uint32_t)j >> 5]);
-        });
-        h = histogram_round<kBins, false>(sm.hist, x + kXD, round++, need, sy);
+        {
+          const uint32_t pre = cut.prefix;
+          src.for_each([&](uint32_t kk, int32_t) {
+            if ((kk != 0u) & ((kk >> 8) == pre)) lds_inc(&sm.h2[kk & 0xffu]);
+          });
+        }
+        ok = histogram_round<256, true, BS>(sm.h2, x + kXHist, round++, need, sy, h);
+        cut = Cut{0, (cut.prefix << 8) | h.bin, kAllPos};
         need -= h.before;
-        const uint32_t hi = h.bin;
-        sm.h2[t] = 0;
-        __syncthreads();
-        src.for_each([&](uint32_t kk, int32_t j) {
-          if ((kk == tau) & (((uint32_t)j >> 5) == hi)) lds_inc(&sm.h2[(uint32_t)j & 31u]);
-        });
-        h = histogram_round<32, false>(sm.h2, x + kXE, round++, need, sy);
-        cut.pos = (int32_t)((hi << 5) | h.bin);
+        if (ok && h.cnt != need) {
+          const uint32_t tau = cut.prefix;
+          clear_bins<kBins, BS>(sm.hist);
+          __syncthreads();
+          src.for_each([&](uint32_t kk, int32_t j) {
+            if ((kk == tau) & (j >= 0)) lds_inc(&sm.hist[(uint32_t)j >> 5]);
+          });
+          ok = histogram_round<kBins, false, BS>(sm.hist, x + kXHist, round++, need, sy, h);
+          need -= h.before;
+          const uint32_t hi = h.bin;
+          if (ok) {
+            if (t < 256) sm.h2[t] = 0u;
+            __syncthreads();
+            src.for_each([&](uint32_t kk, int32_t j) {
+              if ((kk == tau) & (j >= 0) & (((uint32_t)j >> 5) == hi))
+                lds_inc(&sm.h2[(uint32_t)j & 31u]);
+            });
+            ok = histogram_round<32, false, BS>(sm.h2, x + kXHist, round++, need, sy, h);
+            cut.pos = (int32_t)((hi << 5) | h.bin);
+          }
+        }
+      }
+      if (ok) {
+        __syncthreads();  // the last searches' reads of the histogram are done
+        split_emit<kPaged, BS>(
+            src,
+            [T, cut](uint32_t kk, int32_t j) {
+              return ((kk >> 20) == T) & is_selected(cut, kk, j);
+            },
+            em, r.L, k, x, sm);
       }
     }
   }
+  split_finish<kPaged, BS>(em, k, x, S, !ok, sm);
+}
 
-  // One compare per element (ties folded in as in the register path).
-  uint32_t thr;
-  if (cut.pos == kAllPos) {
-    const uint32_t lo = cut.prefix << cut.shift;
-    thr = lo ? lo : 1u;
-  } else {
-    const uint32_t tau = cut.prefix;
-    const int32_t pos = cut.pos;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int32_t j = (v0 + i * kBlock + t) * 4 + c - rem;
-        if ((key[i][c] == tau) & (j <= pos)) key[i][c] = tau + 1u;
+// The split workers of the register kernel: worker w serves work items w,
+// w + W, ... (W workers, the first workgroups of the grid).
+template <bool kPaged>
+__device__ __forceinline__ void split_worker(const Params& p, SmemSplitB<kBigBlock>& sm) {
+  if (!plan_ok(p)) return;
+  int32_t* plan = p.plan;
+  const int64_t R = p.num_rows;
+  const int64_t cap_items = plan_split_cap(R) * kMaxSeg;
+  const int32_t ni = __builtin_amdgcn_readfirstlane(plan[kPlanWordItems]);
+  const uint32_t n_items = (uint32_t)(ni < 0 ? 0 : (ni > cap_items ? cap_items : ni));
+  const int32_t sp = __builtin_amdgcn_readfirstlane(plan[kPlanWordSpin]);
+  const uint32_t spin = sp > 0 ? (uint32_t)sp : kSpinLimit;
+  const int32_t* items = plan + plan_items_word(R);
+  for (uint32_t it = blockIdx.x; it < n_items; it += (uint32_t)p.workers) {
+    const int64_t b = __builtin_amdgcn_readfirstlane(items[2 * it]);
+    const int32_t seg = __builtin_amdgcn_readfirstlane(items[2 * it + 1]);
+    if ((uint64_t)b < (uint64_t)R) {
+      const RowMeta m = row_meta<kPaged>(p, b, true);
+      if (m.split && seg >= 0 && seg < m.nseg) {
+        uint32_t* x =
+            reinterpret_cast<uint32_t*>(plan + plan_xarea_word(R) + (int64_t)m.slot * kXWords);
+        if (m.seg_len == kSegShort)
+          split_segment<kPaged, kSegShort / (4 * kBigBlock)>(p, b, m, seg, x, spin, sm);
+        else
+          split_segment<kPaged, kSegLong / (4 * kBigBlock)>(p, b, m, seg, x, spin, sm);
       }
     }
-    thr = tau + 1u;
-  }
-  uint32_t mine = 0;
-  src.for_each([&](uint32_t kk, int32_t) { mine += (kk >= thr) ? 1u : 0u; });
-  const uint32_t mine_incl = wave_inclusive_sum(mine);
-  if (lane == 63) sm.wave_cnt[w] = mine_incl;
-  __syncthreads();
-  uint32_t slot = mine_incl - mine;
-  uint32_t total = 0;
-  for (int v = 0; v < kWaves; ++v) {
-    const uint32_t c = sm.wave_cnt[v];
-    slot += v < w ? c : 0u;
-    total += c;
-  }
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  const uint32_t dummy = (uint32_t)kMaxK + (uint32_t)t;
-  src.for_each([&](uint32_t kk, int32_t j) {
-    const bool sel = kk >= thr;
-    stage[(sel & (slot < (uint32_t)kMaxK)) ? slot : dummy] = j;
-    slot += sel ? 1u : 0u;
-  });
-  if (t == 0)
-    s_word[0] = __hip_atomic_fetch_add(&x[kXOut], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t base = s_word[0];
-  auto emit = [&](auto value) {
-    for (uint32_t i = t; i < total; i += kBlock) {
-      const int32_t j = stage[i];
-      const bool ok = ((uint32_t)j < (uint32_t)r.L) & (base + i < k);
-      if (ok) em.put(base + i, j, value(j));
-    }
-  };
-  if (kPaged && em.staged)
-    emit([&](int32_t j) { return em.value_lds(j, sm.pt); });
-  else
-    emit([&](int32_t j) { return em.value(j); });
-  __syncthreads();  // s_word is reused below
-  if (t == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint32_t d =
-        __hip_atomic_fetch_add(&x[kXDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_word[0] = d == (uint32_t)S - 1u;
-  }
-  __syncthreads();
-  if (s_word[0]) {
-    // every segment is past its last access: zero what this call used
-    const bool fb =
-        __hip_atomic_load(&x[kXFallback], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-    const int32_t end = fb ? kXWords : kXCand;  // the level-1 histogram, or everything
-    for (int32_t i = t; i < end; i += kBlock)
-      if (i < kXCand || i >= kXB)
-        __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int32_t i = kXFlag + t; i < kXWords; i += kBlock)
-      __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // the next item reuses the LDS
   }
 }
 
-// Long rows planned as split rows: one workgroup per (row, segment) item.
+// Every row of a batch with a score stride above 16384 floats, in one
+// launch (a launch costs about 1.6 us even when its workgroups have
+// nothing to do): 512 threads per row, holding 4, 8 or 16 float4 each by
+// the row's span, or a long row in pieces of 16 float4 per thread. At 80
+// VGPRs three rows share a CU, so one row's searches overlap the others'
+// loads (for spans above 16384, two rows of 1024 threads with 8 float4
+// each ran 10-50% slower). With a plan, the first p.workers workgroups are
+// the split workers.
 template <bool kPaged>
-__global__ __launch_bounds__(kBlock) void rows_split_kernel(const Params p) {
-  if (!plan_ok(p)) return;
-  const int64_t R = p.num_rows;
-  const uint32_t it = blockIdx.x;
-  const int32_t n_items = p.plan[kPlanWordItems];
-  if ((int32_t)it >= n_items || it >= (uint32_t)(plan_split_cap(R) * kMaxSeg)) return;
-  const int32_t* items = p.plan + plan_items_word(R);
-  const int64_t b = items[2 * it];
-  const int32_t seg = items[2 * it + 1];
-  if ((uint64_t)b >= (uint64_t)R) return;
-  const RowInfo r = row_info(p.seq_lens, p.row_starts, p.k, b);
-  if (!split_served(p, b, r)) return;
-  const int32_t S = p.plan[plan_nseg_word(R) + b];
-  if (seg < 0 || seg >= S) return;
-  const int32_t slot = p.plan[plan_slot_word(R) + b];
-  uint32_t* x = reinterpret_cast<uint32_t*>(p.plan + plan_xarea_word(R) + (int64_t)slot * kXWords);
-  __shared__ SmemSplit sm;
-  __shared__ uint32_t s_word[2];
-  segment_in_registers<kPaged>(p, b, r, seg, S, x, sm, s_word);
+__global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) void
+rows_reg_kernel(const Params p) {
+  __shared__ union {
+    SmemRegB<kBigBlock> reg;
+    SmemSplitB<kBigBlock> split;
+    SmemPieces pieces;
+    SmemStream two;
+  } sm;
+  if ((int32_t)blockIdx.x < p.workers) {
+    split_worker<kPaged>(p, sm.split);
+    return;
+  }
+  const int64_t b = (int64_t)blockIdx.x - p.workers;
+  const RowMeta m = row_meta<kPaged>(p, b, true);
+  const RowInfo& r = m.r;
+  // long rows: the split workers' or the streaming kernel's, unless the
+  // plan leaves them to this kernel
+  if (r.cls == kClassLong &&
+      (m.split || p.long_mode == kLongPerRow || (p.long_mode == kLongListed && m.streamed)))
+    return;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
+  if (r.L <= p.k) {
+    write_trivial<kPaged, kBigBlock>(em, r.L, p.k);
+    return;
+  }
+  const RowView rv = row_view(p, b, r);
+  if (r.span <= kBigVec * kBigBlock) {
+    row_in_registers<kBigVec / 4, kPaged, kBigBlock>(rv, p.k, em, sm.reg);
+  } else if (r.span <= kBigVec * 2 * kBigBlock) {
+    row_in_registers<kBigVec / 2, kPaged, kBigBlock>(rv, p.k, em, sm.reg);
+  } else if (r.span <= kBigVec * 4 * kBigBlock) {
+    row_in_registers<kBigVec, kPaged, kBigBlock>(rv, p.k, em, sm.reg);
+  } else if (!row_in_pieces<kPaged>(rv, p.k, em, sm.pieces)) {
+    __syncthreads();
+    row_streaming<kPaged, kBigBlock>(rv, p.k, em, sm.two);
+  }
+}
+
+// Long rows read whole, one 1024-thread workgroup at a time: with no plan
+// one workgroup per row of the batch (the others leave at once); with a
+// plan a persistent grid, workgroup g reading the plan's streamed rows g,
+// g + G, ... (G workgroups), each row during its final cut touching the
+// opening lines of the row it reads next.
+template <bool kPaged>
+__device__ __forceinline__ void long_row(const Params& p, int64_t b, const RowMeta& m,
+                                         const Prefetch pf) {
+  const RowInfo& r = m.r;
+  const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
+  __shared__ union {
+    SmemS1 one;
+    SmemRegB<kLongBlock> fin;
+    SmemStream two;
+  } sm;
+  const RowView rv = row_view(p, b, r);
+  if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
+    __syncthreads();
+    row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);
+  }
+}
+
+template <bool kPaged>
+__global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
+rows_long_kernel(const Params p) {
+  // Workgroup g reads row g of the batch, or with a plan entry g of the
+  // plan's streamed list. (A persistent grid looping over the list would
+  // launch fewer workgroups, but the loop keeps values the compiler hoists
+  // out of it live through the row's body, which spills at the 64 VGPRs of
+  // two workgroups per CU.)
+  const int32_t g = blockIdx.x;
+  int64_t b = g;
+  Prefetch pf{nullptr, 0};
+  if (p.long_mode == kLongListed) {
+    if (!plan_ok(p)) return;
+    const int32_t ns = __builtin_amdgcn_readfirstlane(p.plan[kPlanWordStreamed]);
+    const int32_t off = __builtin_amdgcn_readfirstlane(p.plan[kPlanWordOffset + kClassLong]);
+    const int32_t n = ns < 0 ? 0 : (ns > p.num_rows ? p.num_rows : ns);
+    if (g >= n || off < 0 || off > p.num_rows - n) return;
+    const int32_t* list = p.plan + kPlanHeaderWords + off;
+    b = __builtin_amdgcn_readfirstlane(list[g]);
+    // the listed row likely to start next on this workgroup's XCD
+    if (g + kPrefetchAhead < n) {
+      const int64_t b2 = __builtin_amdgcn_readfirstlane(list[g + kPrefetchAhead]);
+      if ((uint64_t)b2 < (uint64_t)p.num_rows)
+        pf = next_row(p, b2, 0, kClassLong, kS1Depth * kS1Chunk);
+    }
+    if ((uint64_t)b >= (uint64_t)p.num_rows) return;
+  } else {
+    pf = next_row(p, b, kPrefetchAhead, kClassLong, kS1Depth * kS1Chunk);
+  }
+  const RowMeta m = row_meta<kPaged>(p, b, true);
+  if (m.r.cls != kClassLong || m.split) return;
+  if (p.long_mode == kLongListed && !m.streamed) return;
+  long_row<kPaged>(p, b, m, pf);
 }
 
 // Plan: classify every row and list the rows of each class (workgroup 0).
@@ -2165,10 +2574,14 @@ constexpr int kPlanBlock = 1024;
 // batches zero them in a second launch that reads the count from the plan.
 constexpr int kFusedClearRows = kPlanBlock;
 
+// The words of split row q's exchange area that must be zero at the start
+// of a call: the histogram and the counters (the candidate pairs are
+// written before they are read).
 __device__ __forceinline__ void zero_area(int32_t num_rows, int32_t* plan, int32_t q,
                                           int32_t block) {
   int32_t* x = plan + plan_xarea_word(num_rows) + (int64_t)q * kXWords;
-  for (int32_t i = tix(); i < kXWords; i += block) x[i] = 0;
+  for (int32_t i = tix(); i < kXCand; i += block) x[i] = 0;
+  for (int32_t i = kXFlag + tix(); i < kXWords; i += block) x[i] = 0;
 }
 
 __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_lens,
@@ -2196,6 +2609,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   __shared__ uint32_t fill[kNumClasses];
   __shared__ uint32_t n_split;
   __shared__ uint32_t n_items;
+  __shared__ uint32_t n_seg_long;  // segments of the long rows at kSegLong floats
   if (tix() < kNumClasses) {
     count[tix()] = 0;
     fill[tix()] = 0;
@@ -2203,9 +2617,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   if (tix() == 0) {
     n_split = 0;
     n_items = 0;
+    n_seg_long = 0;
   }
   __syncthreads();
-  int32_t* cls = plan + kPlanHeaderWords + num_rows;
+  int32_t* cls = plan + plan_cls_word(num_rows);
   int32_t* nseg = plan + plan_nseg_word(num_rows);
   int32_t* slot = plan + plan_slot_word(num_rows);
   int32_t* items = plan + plan_items_word(num_rows);
@@ -2214,17 +2629,21 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     const RowInfo r = row_info(seq_lens, row_starts, k, b);
     cls[b] = r.cls;
     atomicAdd(&count[r.cls], 1u);
+    if (r.cls == kClassLong) atomicAdd(&n_seg_long, (uint32_t)segments_for(r.span, kSegLong));
   }
   __syncthreads();
-  // the long rows are split all (at most cap of them) or none
+  // the long rows are split all (at most cap of them) or none; in short
+  // segments when long ones would leave CUs idle
   const bool split = count[kClassLong] <= cap;
+  const int32_t seg_len = n_seg_long < (uint32_t)kChipCUs ? kSegShort : kSegLong;
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     int32_t S = 0;
     int32_t q = -1;
     if (split && cls[b] == kClassLong) {
       const RowInfo r = row_info(seq_lens, row_starts, k, b);
-      S = segments_for(r.span);
+      S = segments_for(r.span, seg_len);
       q = (int32_t)atomicAdd(&n_split, 1u);
+      // a row's segments are consecutive work items
       const uint32_t at = atomicAdd(&n_items, (uint32_t)S);
       for (int32_t sg = 0; sg < S; ++sg) {
         items[2 * (at + sg)] = b;
@@ -2255,6 +2674,9 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     plan[kPlanWordSplit] = (int32_t)n_split;
     plan[kPlanWordItems] = (int32_t)n_items;
     plan[kPlanWordError] = 0;
+    plan[kPlanWordSpin] = 0;
+    plan[kPlanWordSegLen] = seg_len;
+    plan[kPlanWordStreamed] = split ? 0 : (int32_t)count[kClassLong];
   }
 }
 
@@ -2302,19 +2724,23 @@ struct KernelLaunch {
   dim3 block;
 };
 
-// The kernels the score stride allows (a row's span never exceeds
-// score_stride), in stream order. A stride up to 8192 floats: every row is
-// short, and the short-row kernel serves the batch alone; up to 16384, the
-// mid kernel alone. Longer strides: one register kernel for every row up
-// to 32768 floats, and above that the streaming kernel for long rows and,
-// with a plan, the split kernel. Each kernel serves the rows of its own
-// classes and skips the others.
+// The kernels for a batch, in stream order, chosen by the score stride (a
+// row's span never exceeds it). Up to 8192 floats every row is short: the
+// short-row kernel (or the wide one, for few rows) serves the batch alone;
+// up to 16384 the mid kernel alone; up to 32768 the register kernel alone.
+// Longer strides: the register kernel, whose first workgroups are the split
+// workers when a plan is given, then the streaming kernel, unless the plan
+// splits every long row (at most kMaxSplitRows rows). Each launch reports
+// its own status.
 template <bool kPaged>
 int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
   const bool lng = p.stride > (int64_t)kBigVec * 4 * kBigBlock;
   if (!lng) p.plan = nullptr;
-  KernelLaunch ls[3];
+  p.workers = 0;
+  p.long_mode = !p.plan ? kLongPerRow
+                        : (p.num_rows > kMaxSplitRows ? kLongListed : kLongInPieces);
+  KernelLaunch ls[2];
   int n = 0;
   if (p.stride <= (int64_t)kSmallVec * 4 * kBlock) {
     if (p.num_rows <= kWideRows)
@@ -2324,14 +2750,22 @@ int launch_rows(Params p, hipStream_t stream) {
   } else if (p.stride <= (int64_t)kLargeVec * 4 * kBlock) {
     ls[n++] = {rows_mid_kernel<kPaged>, grid, dim3(kBlock)};
   } else {
-    if (lng && p.plan)
-      ls[n++] = {rows_split_kernel<kPaged>,
-                 dim3((unsigned)(plan_split_cap(p.num_rows) * kMaxSeg)), dim3(kBlock)};
-    if (lng) ls[n++] = {rows_long_kernel<kPaged>, grid, dim3(kLongBlock)};
-    ls[n++] = {rows_reg_kernel<kPaged>, grid, dim3(kBigBlock)};
+    if (p.plan) {
+      const int64_t w = plan_split_cap(p.num_rows) * kMaxSeg;
+      p.workers = (int32_t)(w < kMaxWorkers ? w : kMaxWorkers);
+    }
+    ls[n++] = {rows_reg_kernel<kPaged>, dim3((unsigned)(p.workers + p.num_rows)),
+               dim3(kBigBlock)};
+    if (lng && p.long_mode != kLongInPieces)
+      ls[n++] = {rows_long_kernel<kPaged>, grid, dim3(kLongBlock)};
   }
-  for (int i = 0; i < n; ++i) ls[i].fn<<<ls[i].grid, ls[i].block, 0, stream>>>(p);
-  return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
+  for (int i = 0; i < n; ++i) {
+    void* args[] = {&p};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(ls[i].fn), ls[i].grid, ls[i].block, args, 0,
+                        stream) != hipSuccess)
+      return DSATOPK_ERR_HIP;
+  }
+  return DSATOPK_OK;
 }
 
 }  // namespace
@@ -2363,12 +2797,33 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
   if ((reinterpret_cast<uintptr_t>(plan) & 15u) != 0) return DSATOPK_ERR_ALIGNMENT;
   const int64_t cap = plan_split_cap(num_rows);
   const bool fused = num_rows <= kFusedClearRows;
-  hipLaunchKernelGGL(plan_kernel, dim3(fused ? (unsigned)(1 + cap) : 1u), dim3(kPlanBlock), 0,
-                     (hipStream_t)stream, seq_lens, row_starts, num_rows, k, (int32_t*)plan);
-  if (!fused)
-    hipLaunchKernelGGL(plan_clear_kernel, dim3((unsigned)cap), dim3(kBlock), 0,
-                       (hipStream_t)stream, num_rows, (int32_t*)plan);
-  return hipGetLastError() == hipSuccess ? DSATOPK_OK : DSATOPK_ERR_HIP;
+  int32_t* pl = static_cast<int32_t*>(plan);
+  {
+    void* args[] = {&seq_lens, &row_starts, &num_rows, &k, &pl};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(plan_kernel),
+                        dim3(fused ? (unsigned)(1 + cap) : 1u), dim3(kPlanBlock), args, 0,
+                        (hipStream_t)stream) != hipSuccess)
+      return DSATOPK_ERR_HIP;
+  }
+  if (!fused) {
+    void* args[] = {&num_rows, &pl};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(plan_clear_kernel), dim3((unsigned)cap),
+                        dim3(kBlock), args, 0, (hipStream_t)stream) != hipSuccess)
+      return DSATOPK_ERR_HIP;
+  }
+  return DSATOPK_OK;
+}
+
+int dsatopk_plan_error(const void* plan, size_t plan_bytes, int32_t* error, void* stream) {
+  if (!plan || !error) return DSATOPK_ERR_INVALID_ARG;
+  if (plan_bytes < (size_t)kPlanHeaderWords * sizeof(int32_t)) return DSATOPK_ERR_PLAN_TOO_SMALL;
+  int32_t w = 0;
+  if (hipMemcpyAsync(&w, static_cast<const int32_t*>(plan) + kPlanWordError, sizeof(w),
+                     hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return DSATOPK_ERR_HIP;
+  *error = w;
+  return DSATOPK_OK;
 }
 
 int dsatopk_paged(const float* scores, int64_t score_stride, const int32_t* seq_lens,

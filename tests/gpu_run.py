@@ -23,7 +23,9 @@ def to_dev(p):
 
 
 def run(p, d=None, use_plan=False, raw=False, canary=True):
-    """Returns (out as numpy [rows, k], canary rows intact?)."""
+    """Returns (out as numpy [rows, k], canary rows intact?). use_plan:
+    False, True, or "stale" (a plan built for the lengths rolled by one row,
+    so long rows meet segment counts that are not theirs)."""
     import torch
 
     import row_top_selection_amd as dt
@@ -32,7 +34,11 @@ def run(p, d=None, use_plan=False, raw=False, canary=True):
     R, k = p.num_rows, p.k
     big = torch.full((R + 2, k), CANARY, dtype=torch.int32, device=d["scores"].device)
     out = big[1:R + 1]
-    plan = dt.plan(d["lens"], k, row_starts=d["starts"]) if use_plan else None
+    plan = None
+    if use_plan == "stale":
+        plan = dt.plan(torch.roll(d["lens"], 1), k, row_starts=d["starts"])
+    elif use_plan:
+        plan = dt.plan(d["lens"], k, row_starts=d["starts"])
     if raw:
         zeros = torch.zeros(R, dtype=torch.int32, device=d["scores"].device)
         dt.ragged(d["scores"], d["lens"], zeros, k, row_starts=d["starts"], plan=plan, out=out)

@@ -93,12 +93,17 @@ def _edge_rows(k):
     return rows
 
 
-@pytest.mark.parametrize("use_plan", [False, True])
+@pytest.mark.parametrize("use_plan", [False, True, "stale"])
 @pytest.mark.parametrize("mode", ["ragged", "paged"])
 @pytest.mark.parametrize("k", [2048, 1000, 7, 1])
 def test_edge_batch(orc, mode, k, use_plan):
+    """Every length class, start residue and value pattern: without a plan
+    (long rows streamed), with the batch's plan (long rows split) and with a
+    plan built for other lengths (long rows the plan does not split are read
+    in register pieces by the register kernel, and rows that defeat the
+    pieces' threshold by its two-pass path)."""
     p = edge_batch(1000 + k, mode, k, _edge_rows(k), name=f"edge_{mode}_k{k}")
-    check(orc, p, use_plan=use_plan, with_raw=not use_plan)
+    check(orc, p, use_plan=use_plan, with_raw=use_plan is False)
 
 
 # Score strides that select each register kernel (a row's span never exceeds
@@ -183,10 +188,28 @@ def _plan_words(plan):
     return plan.cpu().numpy().view(np.int32)
 
 
+# The plan's layout (int32 words), as the library writes it: a 64-word
+# header (word 12 the split rows, 13 their work items, 14 the error word,
+# 15 the poll limit, 16 the segment length, 17 the long rows read whole),
+# then per row its class-list entry, class, segment count and exchange
+# slot, then 2 words per work item (up to 33 per split row), then one
+# 8384-word exchange area per split row (histogram 0..4095, candidate pairs
+# 4096..8191, counters from 8192 on, each on a 128-byte line of its own).
+MAX_SEG = 33
+X_WORDS = 8384
+
+
+def _layout(R):
+    cap = min(R, SPLIT_CAP)
+    items = 64 + 4 * R
+    xarea = (items + 2 * cap * MAX_SEG + 63) // 64 * 64
+    return items, xarea
+
+
 @pytest.mark.parametrize("name", ["paged_long", "paged_mixed"])
 def test_plan_reuse_and_exchange_reset(orc, name):
-    """One plan serves several calls; split rows' exchange areas end zeroed
-    and no segment ever gave up waiting."""
+    """One plan serves several calls; split rows' exchange areas end
+    zeroed and no segment ever gave up waiting."""
     import torch
 
     import row_top_selection_amd as dt
@@ -198,23 +221,88 @@ def test_plan_reuse_and_exchange_reset(orc, name):
     words = _plan_words(plan)
     n_split, n_items = int(words[12]), int(words[13])
     assert n_split > 0 and n_items >= 2 * n_split
+    assert words[16] in (4096, 8192)
     want = expected(orc, p)
     for _ in range(3):
         out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
         torch.cuda.synchronize()
         assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), want, name)
+    assert dt.plan_error(plan) == 0, "a segment gave up waiting for its row"
     words = _plan_words(plan)
-    assert words[14] == 0, "a segment timed out waiting for its row"
-    R = p.num_rows
-    items_word = 64 + 4 * R
-    cap = min(R, SPLIT_CAP)
-    xwords = 16704
-    xarea = (items_word + 2 * cap * 17 + 63) // 64 * 64
-    x = words[xarea: xarea + n_split * xwords].reshape(n_split, xwords)
+    assert words[17] == 0, "every long row of the batch is split"
+    _, xarea = _layout(p.num_rows)
+    x = words[xarea: xarea + n_split * X_WORDS].reshape(n_split, X_WORDS)
     # histograms and counters must be zero again; the candidate pairs
     # (words 4096..8191) are overwritten before they are read
-    assert not x[:, :4096].any(), "level-1 exchange histograms were not left zeroed"
-    assert not x[:, 8192:].any(), "exchange digits / counters were not reset"
+    assert not x[:, :4096].any(), "exchange histograms were not left zeroed"
+    assert not x[:, 8192:].any(), "exchange counters were not reset"
+
+
+def test_split_row_that_gives_up_reads_minus_one(orc):
+    """A plan whose work list leaves out one segment of a split row, with a
+    small poll limit: that row's other segments give up waiting (bounded
+    polls, every kernel exits), the row's outputs are all -1, the plan's
+    error word is set, and every other row is exact. A fresh plan then
+    serves the same batch exactly."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload("paged_long")
+    d = gpu_run.to_dev(p)
+    want = expected(orc, p)
+    plan = dt.plan(d["lens"], p.k)
+    torch.cuda.synchronize()
+    w = torch.from_numpy(_plan_words(plan).copy())
+    items, _ = _layout(p.num_rows)
+    n_items = int(w[13])
+    row_items = [i for i in range(n_items) if int(w[items + 2 * i]) == 3]
+    assert len(row_items) >= 2
+    w[items + 2 * row_items[1]] = -1  # no worker serves this segment
+    w[15] = 4096  # polls before a wait gives up
+    plan.copy_(w.view(torch.uint8).to(plan.device))
+    print("[gpu] split row with a missing segment", flush=True)
+    out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[3] == -1).all(), "the row that lost a segment must read -1"
+    others = [b for b in range(p.num_rows) if b != 3]
+    assert_rows_equal(canonical(got[others], p.seq_lens[others], p.k), want[others], "others")
+    assert dt.plan_error(plan) == 1
+    plan = dt.plan(d["lens"], p.k, out=plan)
+    out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+    torch.cuda.synchronize()
+    assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), want, "fresh plan")
+    assert dt.plan_error(plan) == 0
+
+
+def test_binding_rejects_misplaced_arguments():
+    """The binding refuses arguments the C ABI would misread: a page table
+    that is not int32, and outputs or a plan that are not on the scores'
+    device (nothing is launched)."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    s = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    lens = torch.full((4,), 64, dtype=torch.int32, device="cuda")
+    pt = torch.zeros((4, 1), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        dt.paged(s, lens, pt.long(), 64, 8)
+    with pytest.raises(ValueError):
+        dt.paged(s, lens, pt.cpu(), 64, 8)
+    with pytest.raises(ValueError):
+        dt.paged(s, lens, pt, 64, 8, out=torch.zeros((4, 8), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        dt.paged(s, lens, pt, 64, 8, out_raw=torch.zeros((4, 8), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        dt.paged(s, lens, pt, 64, 8, plan=torch.zeros(dt.plan_bytes(4), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        dt.ragged(s, lens, lens, 8, out=torch.zeros((4, 8), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        dt.ragged(s, lens, lens, 8, plan=torch.zeros(dt.plan_bytes(4), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        dt.plan(lens, 8, out=torch.zeros(dt.plan_bytes(4), dtype=torch.uint8))
 
 
 def test_stale_plan_gives_same_outputs(orc):
@@ -230,7 +318,7 @@ def test_stale_plan_gives_same_outputs(orc):
     out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
     torch.cuda.synchronize()
     assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), expected(orc, p), "stale")
-    assert _plan_words(plan)[14] == 0
+    assert dt.plan_error(plan) == 0
 
 
 @pytest.mark.parametrize("page_size", [1, 2, 4096])
@@ -317,12 +405,13 @@ def test_graph_replay_matches_eager(orc, name):
             assert np.array_equal(got, eager), f"replay {it} differs from the eager call"
         assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p),
                           f"{name} replay {it}")
-    assert _plan_words(plan)[14] == 0, "a segment timed out waiting for its row"
+    assert dt.plan_error(plan) == 0, "a segment gave up waiting for its row"
 
 
 def test_many_long_rows_are_streamed(orc):
     """More long rows than the split path takes: the plan splits none of
-    them and every long row is streamed by one workgroup."""
+    them, lists them all, and every long row is streamed by one
+    workgroup."""
     import torch
 
     import row_top_selection_amd as dt
@@ -332,7 +421,9 @@ def test_many_long_rows_are_streamed(orc):
     d = gpu_run.to_dev(p)
     plan = dt.plan(d["lens"], p.k)
     torch.cuda.synchronize()
-    assert _plan_words(plan)[12] == 0, "no row may be split"
+    words = _plan_words(plan)
+    assert words[12] == 0, "no row may be split"
+    assert words[17] == p.num_rows, "every long row is listed"
     got, ok = gpu_run.run(p, d, use_plan=True)
     assert ok
     assert_rows_equal(canonical(got, p.seq_lens, p.k), expected(orc, p), p.name)
@@ -368,7 +459,7 @@ def test_sustained_launch_sampled_rows(orc, L):
         got = out[idx].cpu().numpy()
         assert_rows_equal(canonical(got, p.seq_lens[rows], p.k), want, f"{name} run {it}")
     words = _plan_words(plan)
-    assert words[14] == 0, "a segment timed out waiting for its row"
+    assert words[14] == 0, "a segment gave up waiting for its row"
     assert (words[12] == n) == (n <= SPLIT_CAP)
 
 
