@@ -63,7 +63,9 @@ enum {
     /* plan_bytes smaller than dsatopk_plan_bytes(num_rows). */
     DSATOPK_ERR_PLAN_TOO_SMALL = 3,
     /* the HIP runtime reported an error (no device, launch failure). */
-    DSATOPK_ERR_HIP = 4
+    DSATOPK_ERR_HIP = 4,
+    /* dsatopk_paged_noalloc: num_rows above DSATOPK_NOALLOC_MAX_ROWS. */
+    DSATOPK_ERR_TOO_LARGE = 5
 };
 
 /* Largest k (runtime value; one build serves every k). The pages bound the
@@ -237,6 +239,36 @@ int dsatopk_paged_packed(const float* scores, int64_t score_stride, const int32_
 int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq_lens,
                    const int32_t* row_starts, const int32_t* out_offsets, int32_t num_rows,
                    int32_t k, void* plan, size_t plan_bytes, int32_t* out, void* stream);
+
+/* Largest batch of dsatopk_paged_noalloc (its plan fits 16 MiB). */
+#define DSATOPK_NOALLOC_MAX_ROWS 262144
+
+/*
+ * dsatopk_paged_noalloc - dsatopk_paged with its plan in the library's own
+ * static device memory, for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments as for dsatopk_paged, without the plan: each call builds the
+ * batch's plan (dsatopk_plan) in a 16 MiB device array of the library, then
+ * runs the PAGED transform with it. Nothing is allocated or freed, by this
+ * call or by anything it calls; the caller passes the inputs and out.
+ *
+ * The array is one per GPU, held by every GPU the library runs on until the
+ * process ends, and shared by every call on that GPU: calls that overlap on
+ * one GPU (several streams or host threads at once) race on it and must be
+ * ordered by the caller. Each call writes the parts of the plan that must
+ * start at zero itself. The first call on a device looks the array's
+ * address up (hipGetSymbolAddress) with that device current; later calls
+ * reuse it.
+ *
+ * Errors: DSATOPK_ERR_TOO_LARGE (num_rows > DSATOPK_NOALLOC_MAX_ROWS,
+ * returned before any HIP call), then as dsatopk_paged. num_rows == 0 is a
+ * no-op.
+ */
+int dsatopk_paged_noalloc(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                          const int32_t* row_starts, const int32_t* page_table,
+                          int64_t page_table_stride, int32_t page_size, int32_t num_rows,
+                          int32_t k, int32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,10 +21,13 @@ STATUS = {
     2: "DSATOPK_ERR_ALIGNMENT",
     3: "DSATOPK_ERR_PLAN_TOO_SMALL",
     4: "DSATOPK_ERR_HIP",
+    5: "DSATOPK_ERR_TOO_LARGE",
 }
 
+NOALLOC_MAX_ROWS = 262144
+
 EXPORTS = ("dsatopk_status_string", "dsatopk_plan_bytes", "dsatopk_plan", "dsatopk_plan_error",
-           "dsatopk_paged", "dsatopk_paged_packed", "dsatopk_ragged")
+           "dsatopk_paged", "dsatopk_paged_packed", "dsatopk_ragged", "dsatopk_paged_noalloc")
 
 
 class DsatopkError(RuntimeError):
@@ -59,6 +62,8 @@ def _lib():
         lib.dsatopk_paged_packed.restype = ctypes.c_int
         lib.dsatopk_ragged.argtypes = [P, i64, P, P, P, i32, i32, P, sz, P, P]
         lib.dsatopk_ragged.restype = ctypes.c_int
+        lib.dsatopk_paged_noalloc.argtypes = [P, i64, P, P, P, i64, i32, i32, i32, P, P]
+        lib.dsatopk_paged_noalloc.restype = ctypes.c_int
         _handle = lib
     return _handle
 
@@ -231,4 +236,29 @@ def ragged(scores, seq_lens, out_offsets, k: int, row_starts=None, plan=None, ou
         rows, int(k), plan_ptr, plan_n, _ptr(out), _stream(stream))
     if st != 0:
         raise DsatopkError(st, "dsatopk_ragged")
+    return out
+
+
+def paged_noalloc(scores, seq_lens, page_table, page_size: int, k: int, row_starts=None,
+                  out=None, stream=None):
+    """PAGED top-k through ``dsatopk_paged_noalloc`` (the plan lives in the
+    library's static device memory; nothing is allocated except ``out`` when
+    it is not given)."""
+    import torch
+
+    scores = _scores(scores)
+    rows = int(scores.shape[0])
+    _vec_i32(seq_lens, rows, "seq_lens", scores)
+    _vec_i32(row_starts, rows, "row_starts", scores)
+    if page_table.dtype != torch.int32:
+        raise ValueError("page_table must be int32")
+    if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.shape[0] != rows:
+        raise ValueError("page_table must be [rows, width] with contiguous columns")
+    _on(page_table, scores, "page_table")
+    out = _out(out, rows, int(k), scores)
+    st = _lib().dsatopk_paged_noalloc(
+        _ptr(scores), scores.stride(0), _ptr(seq_lens), _ptr(row_starts), _ptr(page_table),
+        page_table.stride(0), int(page_size), rows, int(k), _ptr(out), _stream(stream))
+    if st != 0:
+        raise DsatopkError(st, "dsatopk_paged_noalloc")
     return out

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dsatopk.h"
 #include "select_device.h"
 
@@ -2768,6 +2770,33 @@ int launch_rows(Params p, hipStream_t stream) {
   return DSATOPK_OK;
 }
 
+// The plan of dsatopk_paged_noalloc: a file-scope device array (each GPU
+// that loads the library holds its own copy until the process ends). Host
+// code never uses its name as an address: the address comes from
+// hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kNoAllocBytes = size_t(16) << 20;
+static_assert((size_t)plan_words(DSATOPK_NOALLOC_MAX_ROWS) * sizeof(int32_t) <= kNoAllocBytes,
+              "the largest accepted batch's plan fits the static scratch");
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (found on the first call there).
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSATOPK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSATOPK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DSATOPK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2779,6 +2808,8 @@ const char* dsatopk_status_string(int status) {
     case DSATOPK_ERR_ALIGNMENT: return "scores not 16-byte aligned or stride not a multiple of 4";
     case DSATOPK_ERR_PLAN_TOO_SMALL: return "plan buffer too small";
     case DSATOPK_ERR_HIP: return "HIP runtime error";
+    case DSATOPK_ERR_TOO_LARGE:
+      return "num_rows above DSATOPK_NOALLOC_MAX_ROWS (the static scratch of dsatopk_paged_noalloc)";
     default: return "unknown status";
   }
 }
@@ -2884,6 +2915,25 @@ int dsatopk_ragged(const float* scores, int64_t score_stride, const int32_t* seq
   p.out = out;
   p.plan = (int32_t*)plan;
   return launch_rows<false>(p, (hipStream_t)stream);
+}
+
+int dsatopk_paged_noalloc(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                          const int32_t* row_starts, const int32_t* page_table,
+                          int64_t page_table_stride, int32_t page_size, int32_t num_rows,
+                          int32_t k, int32_t* out, void* stream) {
+  if (num_rows > DSATOPK_NOALLOC_MAX_ROWS) return DSATOPK_ERR_TOO_LARGE;
+  int st = check_common(scores, score_stride, seq_lens, num_rows, k, out, nullptr, 0);
+  if (st != DSATOPK_OK || num_rows == 0) return st;
+  if (!page_table || page_table_stride < 1 || !is_pow2(page_size) || page_size > (1 << 20))
+    return DSATOPK_ERR_INVALID_ARG;
+  void* plan = nullptr;
+  st = noalloc_scratch(&plan);
+  if (st != DSATOPK_OK) return st;
+  const size_t bytes = dsatopk_plan_bytes(num_rows);
+  st = dsatopk_plan(seq_lens, row_starts, num_rows, k, plan, bytes, stream);
+  if (st != DSATOPK_OK) return st;
+  return dsatopk_paged(scores, score_stride, seq_lens, row_starts, page_table, page_table_stride,
+                       page_size, num_rows, k, plan, bytes, out, stream);
 }
 
 }  // extern "C"

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.dsatopk_status_string(code)
     assert lib.dsatopk_status_string(99) == b"unknown status"
 
@@ -132,3 +132,16 @@ def test_library_has_no_oracle_dependency():
         if src.suffix in (".py", ".hip", ".h", ".cpp"):
             text = src.read_text()
             assert "oracle" not in text.lower(), src
+
+
+def test_noalloc_rejects_batches_above_its_scratch(lib):
+    """dsatopk_paged_noalloc refuses a batch whose plan would not fit its
+    static scratch, before any HIP call (fake pointers, no GPU needed)."""
+    n = dt.NOALLOC_MAX_ROWS + 1
+    st = lib.dsatopk_paged_noalloc(A16, 64, A16, None, A16, 8, 64, n, 16, A16, None)
+    assert st == 5
+    assert b"NOALLOC_MAX_ROWS" in lib.dsatopk_status_string(5)
+    # the usual argument checks come before any HIP call too
+    assert lib.dsatopk_paged_noalloc(A16, 64, A16, None, None, 8, 64, 4, 16, A16, None) == 1
+    assert lib.dsatopk_paged_noalloc(A4, 64, A16, None, A16, 8, 64, 4, 16, A16, None) == 2
+    assert lib.dsatopk_paged_noalloc(None, 64, None, None, None, 8, 64, 0, 16, None, None) == 0
