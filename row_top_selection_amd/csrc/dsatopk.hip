@@ -906,6 +906,25 @@ __device__ __forceinline__ void stage_selected(const Src& src, Sel sel, uint32_t
   });
 }
 
+// How many register elements of the workgroup have key >= thr (every
+// thread gets the total). wave_cnt is free on entry and again on return.
+template <int BS, class Src>
+__device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
+                                                   uint32_t* wave_cnt) {
+  uint32_t mine = 0;  // this wave's count (scalar)
+  src.for_each([&](uint32_t kk, int32_t) {
+    mine += (uint32_t)__builtin_popcountll(__ballot(kk >= thr));
+  });
+  if (lane_id() == 0) wave_cnt[wave_id()] = mine;
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int v = 0; v < BS / 64; ++v) tot += wave_cnt[v];
+  tot = __builtin_amdgcn_readfirstlane(tot);
+  __syncthreads();
+  return tot;
+}
+
 // The rest of the register path, once the row's vectors are in x (and the
 // caller has staged the page table, if it stages it).
 template <int NV, bool kPaged, int BS>
@@ -1463,25 +1482,6 @@ template <>
 struct HasWaveSums<SmemPieces> {
   static constexpr bool value = true;
 };
-
-// How many register elements of the workgroup have key >= thr (every
-// thread gets the total). wave_cnt is free on entry and again on return.
-template <int BS, class Src>
-__device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
-                                                   uint32_t* wave_cnt) {
-  uint32_t mine = 0;  // this wave's count (scalar)
-  src.for_each([&](uint32_t kk, int32_t) {
-    mine += (uint32_t)__builtin_popcountll(__ballot(kk >= thr));
-  });
-  if (lane_id() == 0) wave_cnt[wave_id()] = mine;
-  __syncthreads();
-  uint32_t tot = 0;
-#pragma unroll
-  for (int v = 0; v < BS / 64; ++v) tot += wave_cnt[v];
-  tot = __builtin_amdgcn_readfirstlane(tot);
-  __syncthreads();
-  return tot;
-}
 
 // Appends the register elements with key >= thr to cand[n ..) in register
 // order (slots at or past CAP are dropped: the caller has checked the
@@ -2510,6 +2510,11 @@ rows_reg_kernel(const Params p) {
   }
 }
 
+// Long rows up to this many float4 per thread of a 1024-thread workgroup
+// are register rows (13: 53248 floats, the most that fits the 64 VGPRs of
+// two workgroups per CU without spills); longer ones are streamed.
+constexpr int kLongRegVec = 13;
+
 // Long rows read whole, one 1024-thread workgroup at a time: with no plan
 // one workgroup per row of the batch (the others leave at once); with a
 // plan a persistent grid, workgroup g reading the plan's streamed rows g,
@@ -2526,6 +2531,10 @@ __device__ __forceinline__ void long_row(const Params& p, int64_t b, const RowMe
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
+  if (r.span <= kLongRegVec * 4 * kLongBlock) {
+    row_in_registers<kLongRegVec, kPaged, kLongBlock>(rv, p.k, em, sm.fin);
+    return;
+  }
   if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
     __syncthreads();
     row_streaming<kPaged, kLongBlock>(rv, p.k, em, sm.two);

@@ -75,7 +75,7 @@ def _edge_rows(k):
     rows = []
     for r in range(4):
         for L in (0, -3, 1, k - 1, k, k + 1, 8189 - r, 8192 - r, 8193 - r, 18432 - r,
-                  18433 - r, 20000, 65537):
+                  18433 - r, 20000, 32768 - r, 32769 - r, 53248 - r, 53249 - r, 65537):
             rows.append((L, r, "normal"))
     for r in range(4):
         for pat in PATTERNS:
