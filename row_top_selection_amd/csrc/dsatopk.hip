@@ -48,9 +48,17 @@ constexpr int kSmallVec = 8;          // float4 per thread: 8192-float spans
 constexpr int kLargeVec = 16;         // float4 per thread: 16384-float spans
 constexpr int kBigBlock = 512;        // threads per big register row
 constexpr int kBigVec = 16;           // float4 per thread of those: 32768-float spans
+constexpr int kBigLds = 4;            // and 4 more per thread in LDS: 40960-float spans
+constexpr int kBigCap = (kBigVec + kBigLds) * 4 * kBigBlock;  // 40960
 constexpr int kStreamVec = 8;         // float4 per thread per streaming chunk
 constexpr int kStreamCandCap = 2048;  // streaming path: threshold-bin pairs in LDS
 constexpr int kPtCap = 512;           // page-table entries staged in LDS
+// 1024-thread rows stage more (their LDS has room): the tables of register
+// rows up to 131072 floats at a page size of 64
+template <int BS>
+constexpr int pt_cap() {
+  return BS >= 1024 ? 2048 : kPtCap;
+}
 
 struct Params {
   const float* scores;
@@ -95,7 +103,9 @@ constexpr int kNumClasses = 4;
 
 // Plan layout (int32 words): a 64-word header; the rows of each class
 // (class order); each row's class, segment count and exchange slot; the
-// (row, segment) work items of split rows; one exchange area per split row.
+// long rows read whole (their own array, at a fixed place, so that a
+// workgroup loads its entry with the header); the (row, segment) work items
+// of split rows; one exchange area per split row.
 constexpr int kPlanMagic = 0x44534b33;  // "DSK3"
 constexpr int kPlanHeaderWords = 64;
 enum PlanWord : int32_t {
@@ -160,7 +170,8 @@ __host__ __device__ constexpr int64_t plan_split_cap(int64_t rows) {
 __host__ __device__ constexpr int64_t plan_cls_word(int64_t rows) { return kPlanHeaderWords + rows; }
 __host__ __device__ constexpr int64_t plan_nseg_word(int64_t rows) { return kPlanHeaderWords + 2 * rows; }
 __host__ __device__ constexpr int64_t plan_slot_word(int64_t rows) { return kPlanHeaderWords + 3 * rows; }
-__host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
+__host__ __device__ constexpr int64_t plan_stream_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
+__host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 5 * rows; }
 __host__ __device__ constexpr int64_t plan_xarea_word(int64_t rows) {
   return (plan_items_word(rows) + 2 * plan_split_cap(rows) * kMaxSeg + 63) / 64 * 64;
 }
@@ -259,7 +270,7 @@ static_assert(kMaxK + kBlock <= kBins, "a split segment's output stage and its d
 template <int BS>
 struct SmemRegB {
   uint32_t hist[kBins];        // every histogram of the row's digits; finally the output stage
-  int32_t pt[kPtCap];          // the row's page-table entries (PAGED)
+  int32_t pt[pt_cap<BS>()];    // the row's page-table entries (PAGED)
   uint32_t wave_cnt[BS / 64];  // per wave: selected elements
   uint32_t bcast[4];           // a bin search's result, when one wave searches
   // per-lane and per-wave running sums of a search shared by all waves
@@ -840,7 +851,7 @@ __device__ __forceinline__ void load_row(const RowView& rv, float4 (&x)[NV]) {
 // them before the LDS store does not also wait for the scores.
 template <int BS>
 constexpr int table_per_thread() {
-  return (kPtCap + BS - 1) / BS;
+  return (pt_cap<BS>() + BS - 1) / BS;
 }
 
 template <bool kPaged, int BS>
@@ -848,7 +859,7 @@ __device__ __forceinline__ void load_table(const Emit<kPaged>& em, int32_t L,
                                            int32_t (&v)[table_per_thread<BS>()]) {
   if constexpr (kPaged) {
     const int2 sp = em.table_span(L);
-    if (sp.y <= kPtCap) {
+    if (sp.y <= pt_cap<BS>()) {
 #pragma unroll
       for (int q = 0; q < table_per_thread<BS>(); ++q) {
         const int32_t e = q * BS + tix();
@@ -863,7 +874,7 @@ __device__ __forceinline__ void store_table(Emit<kPaged>& em, int32_t* lds, int3
                                             const int32_t (&v)[table_per_thread<BS>()]) {
   if constexpr (kPaged) {
     const int2 sp = em.table_span(L);
-    if (sp.y <= kPtCap) {
+    if (sp.y <= pt_cap<BS>()) {
 #pragma unroll
       for (int q = 0; q < table_per_thread<BS>(); ++q) {
         const int32_t e = q * BS + tix();
@@ -925,6 +936,38 @@ __device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
   return tot;
 }
 
+// The cut of a register row whose level-1 histogram is in sm.hist, then
+// the stage and the emit. The selected positions go to LDS (the
+// histogram's space, free after the cut), then one coalesced pass maps and
+// stores the k outputs. Without a partial tie class (the usual case) the
+// selection is key >= thr, and the cut's counts make that at most k
+// elements. With one (several elements hold exactly the k-th key tau and
+// only those at positions <= pos are taken) the rare second form applies,
+// with a guard on the slot.
+template <bool kPaged, int BS, int kPolicy, class Src>
+__device__ __forceinline__ void cut_stage_emit(const Src& src, const Emit<kPaged>& em, int32_t L,
+                                               int32_t k, SmemRegB<BS>& sm) {
+  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  if (cut.pos == kAllPos) {
+    const uint32_t lo = cut.prefix << cut.shift;
+    const uint32_t thr = lo ? lo : 1u;
+    stage_selected<BS, false>(
+        src, [thr](uint32_t kk, int32_t) { return kk >= thr; }, (uint32_t)k, stage, sm);
+  } else {
+    const uint32_t tau = cut.prefix;
+    const int32_t pos = cut.pos;
+    stage_selected<BS, true>(
+        src,
+        [tau, pos](uint32_t kk, int32_t j) {
+          return (kk != 0u) & ((kk > tau) | ((kk == tau) & (j <= pos)));
+        },
+        (uint32_t)k, stage, sm);
+  }
+  __syncthreads();
+  write_stage<kPaged, BS, kPolicy>(em, stage, L, k, sm.pt);
+}
+
 // The rest of the register path, once the row's vectors are in x (and the
 // caller has staged the page table, if it stages it).
 template <int NV, bool kPaged, int BS>
@@ -978,33 +1021,8 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
   if constexpr (BS > kBlock) store_table<kPaged, BS>(em, sm.pt, L, tv);
   __syncthreads();
   const RegSrc<NV, BS> src{key, -rv.rem, ilast};
-  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
-
-  // Stage the selected positions in LDS (the histogram's space, free now),
-  // then one coalesced pass maps and stores the k outputs. Without a
-  // partial tie class (the usual case) the selection is key >= thr, and the
-  // cut's counts make that at most k elements. With one (several elements
-  // hold exactly the k-th key tau and only those at positions <= pos are
-  // taken) the rare second form applies, with a guard on the slot.
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  if (cut.pos == kAllPos) {
-    const uint32_t lo = cut.prefix << cut.shift;
-    const uint32_t thr = lo ? lo : 1u;
-    stage_selected<BS, false>(
-        src, [thr](uint32_t kk, int32_t) { return kk >= thr; }, (uint32_t)k, stage, sm);
-  } else {
-    const uint32_t tau = cut.prefix;
-    const int32_t pos = cut.pos;
-    stage_selected<BS, true>(
-        src,
-        [tau, pos](uint32_t kk, int32_t j) {
-          return (kk != 0u) & ((kk > tau) | ((kk == tau) & (j <= pos)));
-        },
-        (uint32_t)k, stage, sm);
-  }
-  __syncthreads();
-  write_stage<kPaged, BS, (NV == kLargeVec && BS == kBlock) ? kDefaultStore : kStreamingStore>(
-      em, stage, L, k, sm.pt);
+  cut_stage_emit<kPaged, BS, (NV == kLargeVec && BS == kBlock) ? kDefaultStore : kStreamingStore>(
+      src, em, L, k, sm);
 }
 
 template <int NV, bool kPaged, int BS = kBlock>
@@ -1015,6 +1033,126 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
   float4 x[NV];
   load_row<NV, BS>(rv, x);
   row_from_vectors<NV, kPaged, BS>(rv, x, tv, k, em, sm);
+}
+
+// Rows longer than the registers hold: NL more slices of the row, loaded
+// straight into LDS (16 bytes per lane, no VGPRs; the VGPRs are what limits
+// the workgroups per CU) and turned into keys there. Element (i, c) of
+// thread t is aligned index (i * BS + t) * 4 + c for slices i < NV + NL;
+// slice NV + q is lkeys[q * BS + t].
+template <int BS, int NL>
+struct SmemRegL : SmemRegB<BS> {
+  uint4 lkeys[NL * BS];
+};
+
+template <int NV, int NL, int BS>
+struct RegLdsSrc {
+  const uint32_t (&key)[NV][4];
+  const uint4* lkeys;
+  int32_t origin;  // window position of element (0, 0) of thread 0
+  int32_t ilast;   // last slice that holds columns (workgroup-uniform)
+
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    int32_t base = tix() * 4 + origin;
+    asm volatile("" : "+v"(base));
+    int32_t il = ilast;
+    asm volatile("" : "+s"(il));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i <= il) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f(key[i][c], base + i * BS * 4 + c);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      if (NV + q <= il) {
+        const uint4 v = lkeys[q * BS + tix()];
+        const int32_t j = base + (NV + q) * BS * 4;
+        f(v.x, j);
+        f(v.y, j + 1);
+        f(v.z, j + 2);
+        f(v.w, j + 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <int NV, int NL, bool kPaged, int BS>
+__device__ __forceinline__ void row_in_registers_lds(const RowView& rv, int32_t k, Emit<kPaged> em,
+                                                     SmemRegL<BS, NL>& sm) {
+  const int32_t t = tix();
+  const int32_t L = rv.span - rv.rem;
+  const int32_t nvec = (rv.span + 3) >> 2;
+  const int32_t ilast = __builtin_amdgcn_readfirstlane((nvec - 1) / BS);
+  int32_t tv[table_per_thread<BS>()];
+  load_table<kPaged, BS>(em, L, tv);
+  // the LDS slices' loads first (the row's last columns): lane l of wave w
+  // lands at lkeys[q * BS + 64 w + l]
+  {
+    const __amdgpu_buffer_rsrc_t r = row_buffer(rv.base4, nvec);
+    using lds_void = __attribute__((address_space(3))) void;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      if (NV + q <= ilast)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void*)&sm.lkeys[q * BS + wave_id() * 64], 16, ((NV + q) * BS + t) * 16, 0, 0,
+            kStreamingLoad);
+    }
+  }
+  float4 x[NV];
+  load_vectors<NV, BS>(rv.base4, nvec, 0, x);
+  uint32_t key[NV][4];
+  clear_bins<kBins, BS>(sm.hist);
+  __syncthreads();
+  const uint32_t one = opaque_one();
+  // register slices as their loads land (as in row_from_vectors)
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (i <= ilast) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[i][c] = order_key(lane_of(x[i], c));
+      if (i == 0 && t == 0) {
+        if (rv.rem > 0) key[0][0] = 0u;
+        if (rv.rem > 1) key[0][1] = 0u;
+        if (rv.rem > 2) key[0][2] = 0u;
+      }
+      if (i == ilast) {
+        const int32_t a = 4 * (i * BS + t);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (a + c >= rv.span) key[i][c] = 0u;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
+    }
+  }
+  // the LDS slices, once this wave's loads (issued first) have all landed:
+  // each thread turns its own vectors into keys (columns past the span get
+  // key 0) and counts them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    if (NV + q <= ilast) {
+      uint4 v = sm.lkeys[q * BS + t];
+      const int32_t a = 4 * ((NV + q) * BS + t);
+      uint32_t kv[4] = {order_key(__uint_as_float(v.x)), order_key(__uint_as_float(v.y)),
+                        order_key(__uint_as_float(v.z)), order_key(__uint_as_float(v.w))};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kv[c] = a + c < rv.span ? kv[c] : 0u;
+        lds_add(&sm.hist[kv[c] >> 20], one);
+      }
+      sm.lkeys[q * BS + t] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+    }
+  }
+  store_table<kPaged, BS>(em, sm.pt, L, tv);
+  __syncthreads();
+  const RegLdsSrc<NV, NL, BS> src{key, sm.lkeys, -rv.rem, ilast};
+  cut_stage_emit<kPaged, BS, kStreamingStore>(src, em, L, k, sm);
 }
 
 // Span too long for registers: stream it. Pass 1 builds the level-1
@@ -1702,7 +1840,7 @@ __device__ __forceinline__ RowInfo classify(int32_t len, int32_t s, int32_t k) {
   r.span = r.L + (r.s & 3);
   r.cls = (r.L <= k || r.span <= kSmallVec * 4 * kBlock) ? kClassShort
           : (r.span <= kLargeVec * 4 * kBlock)            ? kClassMid
-          : (r.span <= kBigVec * 4 * kBigBlock)           ? kClassBig
+          : (r.span <= kBigCap)                           ? kClassBig
                                                           : kClassLong;
   return r;
 }
@@ -1796,29 +1934,6 @@ __device__ __forceinline__ Emit<kPaged> row_emit(const Params& p, int64_t b, con
     em.offset = m.offset;
   }
   return em;
-}
-
-// The row `ahead` rows on, when it is of class `cls`: its first `cap`
-// floats from the aligned column at or below its start (see kPrefetchAhead
-// for the idea: the workgroups in flight serve `ahead` consecutive rows, so
-// that row starts on this workgroup's XCD about when this one ends).
-// Streamed rows only: touching the next rows of the 8192-float register
-// kernel (2048 rows ahead, 64 MiB of lines against 32 MiB of L2) made its
-// launches half as slow again.
-__device__ __forceinline__ Prefetch next_row(const Params& p, int64_t b, int32_t ahead,
-                                             int32_t cls, int32_t cap) {
-  Prefetch pf{nullptr, 0};
-  if (b + ahead < p.num_rows) {
-    const int64_t b2 = b + ahead;
-    const int32_t l2 = __builtin_amdgcn_readfirstlane(p.seq_lens[b2]);
-    const int32_t s2 = p.row_starts ? __builtin_amdgcn_readfirstlane(p.row_starts[b2]) : 0;
-    const RowInfo r2 = classify(l2, s2, p.k);
-    if (r2.cls == cls) {
-      pf.base = p.scores + b2 * p.stride + (s2 - (s2 & 3));
-      pf.bytes = 4 * (r2.span < cap ? r2.span : cap);
-    }
-  }
-  return pf;
 }
 
 __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const RowInfo& r) {
@@ -2476,6 +2591,7 @@ __global__ __launch_bounds__(kBigBlock) __attribute__((amdgpu_waves_per_eu(6))) 
 rows_reg_kernel(const Params p) {
   __shared__ union {
     SmemRegB<kBigBlock> reg;
+    SmemRegL<kBigBlock, kBigLds> regl;
     SmemSplitB<kBigBlock> split;
     SmemPieces pieces;
     SmemStream two;
@@ -2504,16 +2620,21 @@ rows_reg_kernel(const Params p) {
     row_in_registers<kBigVec / 2, kPaged, kBigBlock>(rv, p.k, em, sm.reg);
   } else if (r.span <= kBigVec * 4 * kBigBlock) {
     row_in_registers<kBigVec, kPaged, kBigBlock>(rv, p.k, em, sm.reg);
+  } else if (r.span <= kBigCap) {
+    row_in_registers_lds<kBigVec, kBigLds, kPaged, kBigBlock>(rv, p.k, em, sm.regl);
   } else if (!row_in_pieces<kPaged>(rv, p.k, em, sm.pieces)) {
     __syncthreads();
     row_streaming<kPaged, kBigBlock>(rv, p.k, em, sm.two);
   }
 }
 
-// Long rows up to this many float4 per thread of a 1024-thread workgroup
-// are register rows (13: 53248 floats, the most that fits the 64 VGPRs of
-// two workgroups per CU without spills); longer ones are streamed.
+// Long rows up to 65536 floats are register rows of a 1024-thread
+// workgroup: 13 float4 per thread in registers (the most that fits the 64
+// VGPRs of two workgroups per CU without spills) and 3 in LDS (the 80 KB of
+// the streaming path's list hold them); longer ones are streamed.
 constexpr int kLongRegVec = 13;
+constexpr int kLongLds = 3;
+constexpr int kLongRegCap = (kLongRegVec + kLongLds) * 4 * kLongBlock;  // 65536
 
 // Long rows read whole, one 1024-thread workgroup at a time: with no plan
 // one workgroup per row of the batch (the others leave at once); with a
@@ -2528,11 +2649,12 @@ __device__ __forceinline__ void long_row(const Params& p, int64_t b, const RowMe
   __shared__ union {
     SmemS1 one;
     SmemRegB<kLongBlock> fin;
+    SmemRegL<kLongBlock, kLongLds> regl;
     SmemStream two;
   } sm;
   const RowView rv = row_view(p, b, r);
-  if (r.span <= kLongRegVec * 4 * kLongBlock) {
-    row_in_registers<kLongRegVec, kPaged, kLongBlock>(rv, p.k, em, sm.fin);
+  if (r.span <= kLongRegCap) {
+    row_in_registers_lds<kLongRegVec, kLongLds, kPaged, kLongBlock>(rv, p.k, em, sm.regl);
     return;
   }
   if (!row_stream1<kPaged, kLongBlock>(rv, p.k, em, sm.one, sm.fin, pf)) {
@@ -2545,34 +2667,49 @@ template <bool kPaged>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
 rows_long_kernel(const Params p) {
   // Workgroup g reads row g of the batch, or with a plan entry g of the
-  // plan's streamed list. (A persistent grid looping over the list would
+  // plan's streamed rows. (A persistent grid looping over the list would
   // launch fewer workgroups, but the loop keeps values the compiler hoists
   // out of it live through the row's body, which spills at the 64 VGPRs of
-  // two workgroups per CU.)
+  // two workgroups per CU.) Every word read before the scores comes in two
+  // round trips: the plan's header words with this workgroup's and the
+  // touched row's entries, then both rows' words.
   const int32_t g = blockIdx.x;
+  const int32_t R = p.num_rows;
   int64_t b = g;
-  Prefetch pf{nullptr, 0};
+  int64_t b2 = g + kPrefetchAhead;  // the row likely to start next on this XCD
   if (p.long_mode == kLongListed) {
-    if (!plan_ok(p)) return;
-    const int32_t ns = __builtin_amdgcn_readfirstlane(p.plan[kPlanWordStreamed]);
-    const int32_t off = __builtin_amdgcn_readfirstlane(p.plan[kPlanWordOffset + kClassLong]);
-    const int32_t n = ns < 0 ? 0 : (ns > p.num_rows ? p.num_rows : ns);
-    if (g >= n || off < 0 || off > p.num_rows - n) return;
-    const int32_t* list = p.plan + kPlanHeaderWords + off;
-    b = __builtin_amdgcn_readfirstlane(list[g]);
-    // the listed row likely to start next on this workgroup's XCD
-    if (g + kPrefetchAhead < n) {
-      const int64_t b2 = __builtin_amdgcn_readfirstlane(list[g + kPrefetchAhead]);
-      if ((uint64_t)b2 < (uint64_t)p.num_rows)
-        pf = next_row(p, b2, 0, kClassLong, kS1Depth * kS1Chunk);
-    }
-    if ((uint64_t)b >= (uint64_t)p.num_rows) return;
-  } else {
-    pf = next_row(p, b, kPrefetchAhead, kClassLong, kS1Depth * kS1Chunk);
+    const int32_t* st = p.plan + plan_stream_word(R);
+    const int32_t* a_n = p.plan + kPlanWordStreamed;
+    const int32_t* a_b = st + g;
+    const int32_t* a_b2 = g + kPrefetchAhead < R ? st + g + kPrefetchAhead : a_n;
+    auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(*a); };
+    int32_t pm = rd(p.plan + kPlanWordMagic), pr = rd(p.plan + kPlanWordRows), n = rd(a_n),
+            e = rd(a_b), e2 = rd(a_b2);
+    asm volatile("" : "+s"(pm), "+s"(pr), "+s"(n), "+s"(e), "+s"(e2));
+    if (pm != kPlanMagic || pr != R || g >= n || n > R) return;
+    b = e;
+    b2 = g + kPrefetchAhead < n ? e2 : -1;
+    if ((uint64_t)b >= (uint64_t)R) return;
   }
+  // the touched row's words, loaded with the row's own
+  const bool t2 = (uint64_t)b2 < (uint64_t)R;
+  const int32_t* a_l2 = t2 ? p.seq_lens + b2 : p.seq_lens + b;
+  const int32_t* a_s2 = (t2 && p.row_starts) ? p.row_starts + b2 : a_l2;
+  int32_t l2 = __builtin_amdgcn_readfirstlane(*a_l2);
+  int32_t s2 = __builtin_amdgcn_readfirstlane(*a_s2);
   const RowMeta m = row_meta<kPaged>(p, b, true);
+  asm volatile("" : "+s"(l2), "+s"(s2));
   if (m.r.cls != kClassLong || m.split) return;
   if (p.long_mode == kLongListed && !m.streamed) return;
+  Prefetch pf{nullptr, 0};
+  if (t2) {
+    const RowInfo r2 = classify(l2, p.row_starts ? s2 : 0, p.k);
+    if (r2.cls == kClassLong) {
+      const int32_t st2 = p.row_starts ? s2 : 0;
+      pf.base = p.scores + b2 * p.stride + (st2 - (st2 & 3));
+      pf.bytes = 4 * (r2.span < kS1Depth * kS1Chunk ? r2.span : kS1Depth * kS1Chunk);
+    }
+  }
   long_row<kPaged>(p, b, m, pf);
 }
 
@@ -2670,9 +2807,12 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
 #pragma unroll
   for (int c = 1; c < kNumClasses; ++c) off[c] = off[c - 1] + count[c - 1];
   int32_t* list = plan + kPlanHeaderWords;
+  int32_t* stream = plan + plan_stream_word(num_rows);
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const int32_t c = cls[b];
-    list[off[c] + atomicAdd(&fill[c], 1u)] = b;
+    const uint32_t at = atomicAdd(&fill[c], 1u);
+    list[off[c] + at] = b;
+    if (c == kClassLong && !split) stream[at] = b;
   }
   if (tix() == 0) {
     plan[kPlanWordMagic] = kPlanMagic;
@@ -2746,7 +2886,7 @@ struct KernelLaunch {
 template <bool kPaged>
 int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
-  const bool lng = p.stride > (int64_t)kBigVec * 4 * kBigBlock;
+  const bool lng = p.stride > (int64_t)kBigCap;
   if (!lng) p.plan = nullptr;
   p.workers = 0;
   p.long_mode = !p.plan ? kLongPerRow

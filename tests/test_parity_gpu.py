@@ -75,7 +75,8 @@ def _edge_rows(k):
     rows = []
     for r in range(4):
         for L in (0, -3, 1, k - 1, k, k + 1, 8189 - r, 8192 - r, 8193 - r, 18432 - r,
-                  18433 - r, 20000, 32768 - r, 32769 - r, 53248 - r, 53249 - r, 65537):
+                  18433 - r, 20000, 32768 - r, 32769 - r, 40960 - r, 40961 - r, 53248 - r,
+                  53249 - r, 65536 - r, 65537 - r):
             rows.append((L, r, "normal"))
     for r in range(4):
         for pat in PATTERNS:
@@ -192,7 +193,8 @@ def _plan_words(plan):
 # header (word 12 the split rows, 13 their work items, 14 the error word,
 # 15 the poll limit, 16 the segment length, 17 the long rows read whole),
 # then per row its class-list entry, class, segment count and exchange
-# slot, then 2 words per work item (up to 33 per split row), then one
+# slot, then the long rows read whole (one word each), then 2 words per
+# work item (up to 33 per split row), then one
 # 8384-word exchange area per split row (histogram 0..4095, candidate pairs
 # 4096..8191, counters from 8192 on, each on a 128-byte line of its own).
 MAX_SEG = 33
@@ -201,7 +203,7 @@ X_WORDS = 8384
 
 def _layout(R):
     cap = min(R, SPLIT_CAP)
-    items = 64 + 4 * R
+    items = 64 + 5 * R
     xarea = (items + 2 * cap * MAX_SEG + 63) // 64 * 64
     return items, xarea
 
