@@ -1088,21 +1088,35 @@ __device__ __forceinline__ void row_in_registers_lds(const RowView& rv, int32_t 
   const int32_t L = rv.span - rv.rem;
   const int32_t nvec = (rv.span + 3) >> 2;
   const int32_t ilast = __builtin_amdgcn_readfirstlane((nvec - 1) / BS);
-  int32_t tv[table_per_thread<BS>()];
-  load_table<kPaged, BS>(em, L, tv);
   // the LDS slices' loads first (the row's last columns): lane l of wave w
-  // lands at lkeys[q * BS + 64 w + l]
+  // lands at lkeys[q * BS + 64 w + l]. Every slice's load takes the same
+  // VGPR offset (this thread's 16 bytes) in a buffer that starts at the
+  // slice: when the offset VGPR was rewritten between them, the compiler
+  // drained every load in flight before the next slice's (one memory round
+  // trip per slice instead of one for all).
   {
-    const __amdgpu_buffer_rsrc_t r = row_buffer(rv.base4, nvec);
+    // Nothing of this row is in flight yet: this wait (vmcnt 0, the other
+    // counters left alone) costs nothing, and it tells the compiler so. A
+    // load that another path leaves pending into a register it reuses here
+    // would otherwise make it drain the row's own loads at every reuse.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     using lds_void = __attribute__((address_space(3))) void;
+    const int32_t off = t * 16;
+    // the wave's index straight from the thread index (no VGPR copy that
+    // the compiler might place in a register a load in flight still writes)
+    const int32_t w = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      if (NV + q <= ilast)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (lds_void*)&sm.lkeys[q * BS + wave_id() * 64], 16, ((NV + q) * BS + t) * 16, 0, 0,
-            kStreamingLoad);
+      if (NV + q <= ilast) {
+        const int32_t v0 = (NV + q) * BS;  // the slice's first vector
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(row_buffer(rv.base4 + v0, nvec - v0),
+                                                 (lds_void*)&sm.lkeys[q * BS + w * 64], 16, off,
+                                                 0, 0, kStreamingLoad);
+      }
     }
   }
+  int32_t tv[table_per_thread<BS>()];
+  load_table<kPaged, BS>(em, L, tv);
   float4 x[NV];
   load_vectors<NV, BS>(rv.base4, nvec, 0, x);
   uint32_t key[NV][4];
