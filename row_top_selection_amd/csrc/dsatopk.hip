@@ -1028,6 +1028,10 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
 template <int NV, bool kPaged, int BS = kBlock>
 __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
                                                  SmemRegB<BS>& sm) {
+  // Nothing of this row is in flight: this wait costs nothing and keeps the
+  // compiler from draining the table load before the score loads (a load
+  // another path leaves pending into a register it reuses here).
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   int32_t tv[table_per_thread<BS>()];
   load_table<kPaged, BS>(em, rv.span - rv.rem, tv);
   float4 x[NV];
@@ -1864,6 +1868,16 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* seq_lens, const int32
   return classify(seq_lens[b], row_starts ? row_starts[b] : 0, k);
 }
 
+// A word that no kernel of this library writes while it runs (row lengths
+// and starts, table rows and starts, out offsets, the plan's header, row
+// entries and work items), read as constant memory: a scalar load through
+// the scalar cache. The compiler issues such loads together, where vector
+// loads of these words, under register pressure, went through one VGPR and
+// each waited for the one before.
+__device__ __forceinline__ int32_t ld_const(const int32_t* a) {
+  return *(const __attribute__((address_space(4))) int32_t*)a;
+}
+
 // Every word a row's workgroup reads before its scores, loaded together:
 // one memory round trip before the first score load instead of a chain of
 // dependent ones (under a full-chip load each round trip costs
@@ -1900,7 +1914,7 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   const int32_t* a_pc = hp ? p.plan + plan_cls_word(p.num_rows) + b : a_len;
   // (readfirstlane: a no-op on scalar loads; a vector load, where the
   // compiler cannot prove the words unchanged, still ends in an SGPR)
-  auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(*a); };
+  auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(ld_const(a)); };
   int32_t len = rd(a_len), rs = rd(a_rs), tr = rd(a_tr), ts = rd(a_ts), of = rd(a_of);
   int32_t pm = rd(a_pm), pr = rd(a_pr), pg = rd(a_pg), ps = rd(a_ps), pl = rd(a_pl),
           pc = rd(a_pc);
@@ -1959,12 +1973,6 @@ __device__ __forceinline__ RowView row_view(const Params& p, int64_t b, const Ro
   return rv;
 }
 
-// Whether a plan was built for this many rows (only the split kernel and
-// the long-row kernel read it: the split rows' schedule and exchange
-// areas).
-__device__ __forceinline__ bool plan_ok(const Params& p) {
-  return p.plan && p.plan[kPlanWordMagic] == kPlanMagic && p.plan[kPlanWordRows] == p.num_rows;
-}
 
 
 // Trivial rows and spans <= 8192 floats, kept in registers.
@@ -2565,18 +2573,22 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
 // w + W, ... (W workers, the first workgroups of the grid).
 template <bool kPaged>
 __device__ __forceinline__ void split_worker(const Params& p, SmemSplitB<kBigBlock>& sm) {
-  if (!plan_ok(p)) return;
+  if (!p.plan) return;
   int32_t* plan = p.plan;
   const int64_t R = p.num_rows;
   const int64_t cap_items = plan_split_cap(R) * kMaxSeg;
-  const int32_t ni = __builtin_amdgcn_readfirstlane(plan[kPlanWordItems]);
+  // the header words in one round trip
+  const int32_t pm = __builtin_amdgcn_readfirstlane(ld_const(plan + kPlanWordMagic));
+  const int32_t pr = __builtin_amdgcn_readfirstlane(ld_const(plan + kPlanWordRows));
+  const int32_t ni = __builtin_amdgcn_readfirstlane(ld_const(plan + kPlanWordItems));
+  const int32_t sp = __builtin_amdgcn_readfirstlane(ld_const(plan + kPlanWordSpin));
+  if (pm != kPlanMagic || pr != p.num_rows) return;
   const uint32_t n_items = (uint32_t)(ni < 0 ? 0 : (ni > cap_items ? cap_items : ni));
-  const int32_t sp = __builtin_amdgcn_readfirstlane(plan[kPlanWordSpin]);
   const uint32_t spin = sp > 0 ? (uint32_t)sp : kSpinLimit;
   const int32_t* items = plan + plan_items_word(R);
   for (uint32_t it = blockIdx.x; it < n_items; it += (uint32_t)p.workers) {
-    const int64_t b = __builtin_amdgcn_readfirstlane(items[2 * it]);
-    const int32_t seg = __builtin_amdgcn_readfirstlane(items[2 * it + 1]);
+    const int64_t b = __builtin_amdgcn_readfirstlane(ld_const(items + 2 * it));
+    const int32_t seg = __builtin_amdgcn_readfirstlane(ld_const(items + 2 * it + 1));
     if ((uint64_t)b < (uint64_t)R) {
       const RowMeta m = row_meta<kPaged>(p, b, true);
       if (m.split && seg >= 0 && seg < m.nseg) {
@@ -2696,7 +2708,7 @@ rows_long_kernel(const Params p) {
     const int32_t* a_n = p.plan + kPlanWordStreamed;
     const int32_t* a_b = st + g;
     const int32_t* a_b2 = g + kPrefetchAhead < R ? st + g + kPrefetchAhead : a_n;
-    auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(*a); };
+    auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(ld_const(a)); };
     int32_t pm = rd(p.plan + kPlanWordMagic), pr = rd(p.plan + kPlanWordRows), n = rd(a_n),
             e = rd(a_b), e2 = rd(a_b2);
     asm volatile("" : "+s"(pm), "+s"(pr), "+s"(n), "+s"(e), "+s"(e2));
@@ -2709,8 +2721,8 @@ rows_long_kernel(const Params p) {
   const bool t2 = (uint64_t)b2 < (uint64_t)R;
   const int32_t* a_l2 = t2 ? p.seq_lens + b2 : p.seq_lens + b;
   const int32_t* a_s2 = (t2 && p.row_starts) ? p.row_starts + b2 : a_l2;
-  int32_t l2 = __builtin_amdgcn_readfirstlane(*a_l2);
-  int32_t s2 = __builtin_amdgcn_readfirstlane(*a_s2);
+  int32_t l2 = __builtin_amdgcn_readfirstlane(ld_const(a_l2));
+  int32_t s2 = __builtin_amdgcn_readfirstlane(ld_const(a_s2));
   const RowMeta m = row_meta<kPaged>(p, b, true);
   asm volatile("" : "+s"(l2), "+s"(s2));
   if (m.r.cls != kClassLong || m.split) return;
