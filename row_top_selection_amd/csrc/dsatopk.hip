@@ -157,8 +157,7 @@ enum XWord : int32_t {
   kXCand = 4096,    // kCandCapG (key, position) pairs of the level-1 bin
   kXFlag = 8192,    // 64-bit: last published round and its result
   kXArrive = 8224,  // segments arrived (all rounds)
-  kXNCand = 8256,   // candidate pairs written
-  kXOut = 8288,     // output slots taken
+  kXOut = 8288,     // 64-bit: output slots taken (low), candidate pairs written (high)
   kXDone = 8320,    // segments finished
   kXFail = 8352,    // a segment of the row gave up waiting
   kXWords = 8384,   // multiple of 64 words (256 bytes)
@@ -2140,12 +2139,17 @@ struct SplitSync {
 // One histogram round: every segment adds its local LDS histogram (NB
 // bins) into the row's global one; the last to arrive gathers the totals
 // into its LDS (one coalesced read), finds the bin where the running count
-// reaches `need`, zeroes the global bins it found set (the next round reuses
-// them) and publishes. False when the wait gave up.
+// reaches `need`, zeroes the global bins it found set and publishes. A
+// later round adds into the same bins, so they are zero before the publish
+// when one may follow; when none can (the bin is taken whole, or it holds
+// at most later_cap elements, which go to the candidate buffer instead) the
+// zeroing follows the publish, off the other segments' path. False when the
+// wait gave up.
 template <int NB, bool kDesc, int BS>
 __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
                                                 uint32_t round, uint32_t need,
-                                                const SplitSync& sy, BinHit& hit) {
+                                                uint32_t later_cap, const SplitSync& sy,
+                                                BinHit& hit) {
   const int32_t t = tix();
   __syncthreads();  // local histogram complete
   for (int32_t i = t; i < NB; i += BS) {
@@ -2158,10 +2162,17 @@ __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_
     for (int32_t i = t; i < NB; i += BS)
       lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    mine = pack_hit(wave_find<NB, kDesc>(lds_hist, need));
-    for (int32_t i = t; i < NB; i += BS)
-      if (lds_hist[i]) __hip_atomic_store(&g_hist[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const BinHit f = wave_find<NB, kDesc>(lds_hist, need);
+    mine = pack_hit(f);
+    auto zero = [&]() {
+      for (int32_t i = t; i < NB; i += BS)
+        if (lds_hist[i])
+          __hip_atomic_store(&g_hist[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    const bool later = (f.cnt != need - f.before) && (f.cnt > later_cap);
+    if (later) zero();
     sy.publish(round, mine);
+    if (!later) zero();
   }
   uint64_t res;
   const bool ok = sy.result(round, last, mine, res);
@@ -2329,6 +2340,82 @@ __device__ __forceinline__ void split_emit(const Src& src, Sel sel, const Emit<k
   __syncthreads();  // the stage and wave_cnt are free again
 }
 
+// The winners of a segment (keys above the threshold bin T) to the row's
+// output, and the bin's elements (the candidates) to the row's candidate
+// buffer: one counting pass for both, and one 64-bit atomic on the words
+// kXOut (output slots, low half) and kXOut + 1 (candidate slots, high half)
+// takes both ranges. The winners go through the LDS stage as in
+// split_emit; the candidates are stored straight from the registers.
+template <bool kPaged, int BS, class Src>
+__device__ __forceinline__ void split_emit_cands(const Src& src, uint32_t T,
+                                                 const Emit<kPaged>& em, int32_t L, uint32_t k,
+                                                 uint32_t* x, SmemSplitB<BS>& sm) {
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int32_t t = tix();
+  auto win = [T](uint32_t kk) { return (kk != 0u) & ((kk >> 20) > T); };
+  auto cand = [T](uint32_t kk) { return (kk != 0u) & ((kk >> 20) == T); };
+  uint32_t mw = 0, mc = 0;
+  src.for_each([&](uint32_t kk, int32_t) {
+    mw = add_lane_bit(mw, __ballot(win(kk)));
+    mc = add_lane_bit(mc, __ballot(cand(kk)));
+  });
+  const uint32_t iw = wave_inclusive_sum(mw);
+  const uint32_t ic = wave_inclusive_sum(mc);
+  if (lane == 63) {
+    sm.wave_cnt[w] = iw;
+    sm.tie[w] = ic;  // (the tie positions' space is free until a resolve)
+  }
+  __syncthreads();
+  const uint32_t cw = lane < BS / 64 ? sm.wave_cnt[lane] : 0u;
+  const uint32_t cc = lane < BS / 64 ? sm.tie[lane] : 0u;
+  const uint32_t sw = wave_inclusive_sum(cw);
+  const uint32_t sc = wave_inclusive_sum(cc);
+  uint32_t slot = iw - mw + (w ? read_lane(sw, w - 1) : 0u);
+  uint32_t at = ic - mc + (w ? read_lane(sc, w - 1) : 0u);
+  const uint32_t tw = read_lane(sw, BS / 64 - 1);
+  const uint32_t tc = read_lane(sc, BS / 64 - 1);
+  if (t == 0) {
+    const uint64_t add = (uint64_t)tw | ((uint64_t)tc << 32);
+    const uint64_t got =
+        add ? __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(x + kXOut), add,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : 0ull;
+    sm.word[5] = (uint32_t)got;
+    sm.word[6] = (uint32_t)(got >> 32);
+  }
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = win(kk);
+    const uint64_t m = __ballot(s);
+    if (s & (slot < (uint32_t)kMaxK)) stage[slot] = j;
+    slot = add_lane_bit(slot, m);
+  });
+  __syncthreads();
+  const uint32_t base = __builtin_amdgcn_readfirstlane(sm.word[5]);
+  at += __builtin_amdgcn_readfirstlane(sm.word[6]);
+  uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool s = cand(kk);
+    const uint64_t m = __ballot(s);
+    if (s & (at < (uint32_t)kCandCapG))
+      __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    at = add_lane_bit(at, m);
+  });
+  auto put = [&](auto value) {
+    for (uint32_t i = (uint32_t)t; i < tw; i += BS) {
+      const int32_t j = stage[i];
+      if (((uint32_t)j < (uint32_t)L) & (base + i < k)) em.put((int32_t)(base + i), j, value(j));
+    }
+  };
+  if (kPaged && em.staged)
+    put([&](int32_t j) { return em.value_lds(j, sm.pt); });
+  else
+    put([&](int32_t j) { return em.value(j); });
+  __syncthreads();  // the stage and wave_cnt are free again
+}
+
 // -1 in every output slot of the row (a row whose segments gave up).
 template <bool kPaged, int BS>
 __device__ __forceinline__ void split_fail_row(const Emit<kPaged>& em, uint32_t k) {
@@ -2431,61 +2518,30 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
   }
   uint32_t round = 1;
   BinHit h;
-  bool ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, k, sy, h);
+  bool ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, k, kCandCapG, sy, h);
   if (ok) {
     uint32_t need = k - h.before;
     const uint32_t T = h.bin;
     const bool whole = h.cnt == need;
-    // the winners above the threshold bin (with it, when it is taken whole)
-    split_emit<kPaged, BS>(
-        src,
-        [T, whole](uint32_t kk, int32_t) {
-          const uint32_t d = kk >> 20;
-          return (kk != 0u) & ((d > T) | (whole & (d == T)));
-        },
-        em, r.L, k, x, sm);
     if (!whole && h.cnt <= (uint32_t)kCandCapG) {
-      // the bin's elements to the row's candidate buffer
-      uint32_t mine = 0;
-      src.for_each([&](uint32_t kk, int32_t) { mine += ((kk != 0u) & ((kk >> 20) == T)) ? 1u : 0u; });
-      const uint32_t incl = wave_inclusive_sum(mine);
-      if (lane == 63) sm.wave_cnt[w] = incl;
-      __syncthreads();
-      const uint32_t c = lane < BS / 64 ? sm.wave_cnt[lane] : 0u;
-      const uint32_t ic = wave_inclusive_sum(c);
-      const uint32_t pre = incl - mine + (w ? read_lane(ic, w - 1) : 0u);
-      const uint32_t tot = read_lane(ic, BS / 64 - 1);
-      if (t == 0)
-        sm.word[5] = tot ? __hip_atomic_fetch_add(&x[kXNCand], tot, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                         : 0u;
-      __syncthreads();
-      uint32_t at = __builtin_amdgcn_readfirstlane(sm.word[5]) + pre;
-      uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
-      src.for_each([&](uint32_t kk, int32_t j) {
-        if ((kk != 0u) & ((kk >> 20) == T)) {
-          if (at < (uint32_t)kCandCapG)
-            __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          ++at;
-        }
-      });
+      // the winners above the bin to the output and the bin's elements to
+      // the row's candidate buffer
+      split_emit_cands<kPaged, BS>(src, T, em, r.L, k, x, sm);
       if (sy.arrive(round++)) {
         // the last segment: every candidate is in; resolve and emit them
         const uint32_t n = h.cnt;
+        const uint64_t* gcand = reinterpret_cast<const uint64_t*>(x + kXCand);
         uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // kCandCapG pairs fill the histogram
         for (uint32_t i = (uint32_t)t; i < n; i += BS) {
           const uint64_t e = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
         }
-        if (t == 0) {
-          sm.word[5] =
-              __hip_atomic_fetch_add(&x[kXOut], need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          sm.word[6] = 0u;
-        }
+        if (t == 0) sm.word[6] = 0u;
         __syncthreads();
         const Cut cut = resolve_pairs_group<BS>(lcand, n, need, sm);
-        const uint32_t base = __builtin_amdgcn_readfirstlane(sm.word[5]);
+        // the segments' winners above the bin number h.before (the merged
+        // count): they took slots [0, h.before), the bin's take the rest
+        const uint32_t base = h.before;
         auto put = [&](auto value) {
           for (uint32_t i0 = 0; i0 < n; i0 += BS) {
             const uint32_t i = i0 + (uint32_t)t;
@@ -2509,7 +2565,17 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
         // this segment's entries)
         put([&](int32_t j) { return em.value(j); });
       }
-    } else if (!whole) {
+    } else {
+      // the winners above the threshold bin (with it, when it is taken whole)
+      split_emit<kPaged, BS>(
+          src,
+          [T, whole](uint32_t kk, int32_t) {
+            const uint32_t d = kk >> 20;
+            return (kk != 0u) & ((d > T) | (whole & (d == T)));
+          },
+          em, r.L, k, x, sm);
+    }
+    if (!whole && h.cnt > (uint32_t)kCandCapG) {
       // The bin is too large for the buffer: one merged round per digit.
       clear_bins<kBins, BS>(sm.hist);
       __syncthreads();
@@ -2518,7 +2584,7 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
           if ((kk != 0u) & ((kk >> 20) == T)) lds_inc(&sm.hist[(kk >> 8) & 0xfffu]);
         });
       }
-      ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, need, sy, h);
+      ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, need, 0u, sy, h);
       Cut cut{8, (T << 12) | h.bin, kAllPos};
       need -= h.before;
       if (ok && h.cnt != need) {
@@ -2530,7 +2596,7 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
             if ((kk != 0u) & ((kk >> 8) == pre)) lds_inc(&sm.h2[kk & 0xffu]);
           });
         }
-        ok = histogram_round<256, true, BS>(sm.h2, x + kXHist, round++, need, sy, h);
+        ok = histogram_round<256, true, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, h);
         cut = Cut{0, (cut.prefix << 8) | h.bin, kAllPos};
         need -= h.before;
         if (ok && h.cnt != need) {
@@ -2540,7 +2606,7 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
           src.for_each([&](uint32_t kk, int32_t j) {
             if ((kk == tau) & (j >= 0)) lds_inc(&sm.hist[(uint32_t)j >> 5]);
           });
-          ok = histogram_round<kBins, false, BS>(sm.hist, x + kXHist, round++, need, sy, h);
+          ok = histogram_round<kBins, false, BS>(sm.hist, x + kXHist, round++, need, 0u, sy, h);
           need -= h.before;
           const uint32_t hi = h.bin;
           if (ok) {
@@ -2550,7 +2616,7 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
               if ((kk == tau) & (j >= 0) & (((uint32_t)j >> 5) == hi))
                 lds_inc(&sm.h2[(uint32_t)j & 31u]);
             });
-            ok = histogram_round<32, false, BS>(sm.h2, x + kXHist, round++, need, sy, h);
+            ok = histogram_round<32, false, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, h);
             cut.pos = (int32_t)((hi << 5) | h.bin);
           }
         }
