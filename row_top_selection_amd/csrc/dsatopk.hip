@@ -2149,7 +2149,7 @@ template <int NB, bool kDesc, int BS>
 __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_hist,
                                                 uint32_t round, uint32_t need,
                                                 uint32_t later_cap, const SplitSync& sy,
-                                                BinHit& hit) {
+                                                SmemSplitB<BS>& sm, BinHit& hit) {
   const int32_t t = tix();
   __syncthreads();  // local histogram complete
   for (int32_t i = t; i < NB; i += BS) {
@@ -2162,7 +2162,8 @@ __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_
     for (int32_t i = t; i < NB; i += BS)
       lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const BinHit f = wave_find<NB, kDesc>(lds_hist, need);
+    // (4096 bins: every wave searches a part; fewer: one wave each)
+    const BinHit f = group_find<NB, kDesc, BS>(lds_hist, need, sm);
     mine = pack_hit(f);
     auto zero = [&]() {
       for (int32_t i = t; i < NB; i += BS)
@@ -2518,7 +2519,8 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
   }
   uint32_t round = 1;
   BinHit h;
-  bool ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, k, kCandCapG, sy, h);
+  bool ok =
+      histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, k, kCandCapG, sy, sm, h);
   if (ok) {
     uint32_t need = k - h.before;
     const uint32_t T = h.bin;
@@ -2532,38 +2534,63 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
         const uint32_t n = h.cnt;
         const uint64_t* gcand = reinterpret_cast<const uint64_t*>(x + kXCand);
         uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // kCandCapG pairs fill the histogram
-        for (uint32_t i = (uint32_t)t; i < n; i += BS) {
-          const uint64_t e = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+        // Each thread's candidates (i = t + s BS) and their emitted values:
+        // the page-table lookups are issued now and land during the resolve.
+        constexpr int kCandPer = kCandCapG / BS;
+        int32_t cval[kCandPer];
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+          const uint32_t i = (uint32_t)(q * BS + t);
+          cval[q] = 0;
+          if (i < n) {
+            const uint64_t e =
+                __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+            const int32_t j = (int32_t)(e >> 32);
+            if ((uint32_t)j < (uint32_t)r.L) cval[q] = em.value(j);
+          }
         }
+        // Every segment of the row has arrived, so none gave up: this one
+        // counts itself done now (issued after its loads, so their waits do
+        // not wait for it) and reads the count at the end, the round trip
+        // hidden behind the resolve. Nothing after this touches the words
+        // a last finisher resets.
+        uint32_t done_prev = 0u;
+        if (t == 0)
+          done_prev =
+              __hip_atomic_fetch_add(&x[kXDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (t == 0) sm.word[6] = 0u;
         __syncthreads();
         const Cut cut = resolve_pairs_group<BS>(lcand, n, need, sm);
         // the segments' winners above the bin number h.before (the merged
         // count): they took slots [0, h.before), the bin's take the rest
         const uint32_t base = h.before;
-        auto put = [&](auto value) {
-          for (uint32_t i0 = 0; i0 < n; i0 += BS) {
-            const uint32_t i = i0 + (uint32_t)t;
-            const uint2 e = i < n ? lcand[i] : make_uint2(0u, 0u);
-            const bool s = (i < n) && is_selected(cut, e.x, (int32_t)e.y);
-            const uint64_t mm = __ballot(s);
-            if (mm == 0) continue;
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
-            const int leader = __builtin_ctzll(mm);
-            uint32_t wb = 0;
-            if (lane == leader) wb = atomicAdd(&sm.word[6], (uint32_t)__builtin_popcountll(mm));
-            wb = read_lane(wb, leader);
-            const uint32_t slot = wb + rank;
-            const int32_t j = (int32_t)e.y;
-            if (s & (slot < need) & ((uint32_t)j < (uint32_t)r.L) & (base + slot < k))
-              em.put((int32_t)(base + slot), j, value(j));
-          }
-        };
-        // (candidates come from every segment: the LDS table holds only
-        // this segment's entries)
-        put([&](int32_t j) { return em.value(j); });
+#pragma unroll
+        for (int q = 0; q < kCandPer; ++q) {
+          const uint32_t i = (uint32_t)(q * BS + t);
+          const uint2 e = i < n ? lcand[i] : make_uint2(0u, 0u);
+          const bool s = (i < n) && is_selected(cut, e.x, (int32_t)e.y);
+          const uint64_t mm = __ballot(s);
+          if (mm == 0) continue;
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+          const int leader = __builtin_ctzll(mm);
+          uint32_t wb = 0;
+          if (lane == leader) wb = atomicAdd(&sm.word[6], (uint32_t)__builtin_popcountll(mm));
+          wb = read_lane(wb, leader);
+          const uint32_t slot = wb + rank;
+          const int32_t j = (int32_t)e.y;
+          if (s & (slot < need) & ((uint32_t)j < (uint32_t)r.L) & (base + slot < k))
+            em.put((int32_t)(base + slot), j, cval[q]);
+        }
+        if (t == 0) sm.word[0] = done_prev == (uint32_t)S - 1u;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(sm.word[0]) != 0u) {
+          // the row's last segment to finish: reset the counters
+          for (int32_t i = kXFlag + t; i < kXWords; i += BS)
+            __hip_atomic_store(&x[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;  // counted done above
       }
     } else {
       // the winners above the threshold bin (with it, when it is taken whole)
@@ -2584,7 +2611,8 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
           if ((kk != 0u) & ((kk >> 20) == T)) lds_inc(&sm.hist[(kk >> 8) & 0xfffu]);
         });
       }
-      ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, need, 0u, sy, h);
+      ok = histogram_round<kBins, true, BS>(sm.hist, x + kXHist, round++, need, 0u, sy, sm,
+                                            h);
       Cut cut{8, (T << 12) | h.bin, kAllPos};
       need -= h.before;
       if (ok && h.cnt != need) {
@@ -2596,7 +2624,7 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
             if ((kk != 0u) & ((kk >> 8) == pre)) lds_inc(&sm.h2[kk & 0xffu]);
           });
         }
-        ok = histogram_round<256, true, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, h);
+        ok = histogram_round<256, true, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, sm, h);
         cut = Cut{0, (cut.prefix << 8) | h.bin, kAllPos};
         need -= h.before;
         if (ok && h.cnt != need) {
@@ -2606,7 +2634,8 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
           src.for_each([&](uint32_t kk, int32_t j) {
             if ((kk == tau) & (j >= 0)) lds_inc(&sm.hist[(uint32_t)j >> 5]);
           });
-          ok = histogram_round<kBins, false, BS>(sm.hist, x + kXHist, round++, need, 0u, sy, h);
+          ok = histogram_round<kBins, false, BS>(sm.hist, x + kXHist, round++, need, 0u, sy,
+                                                 sm, h);
           need -= h.before;
           const uint32_t hi = h.bin;
           if (ok) {
@@ -2616,7 +2645,8 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
               if ((kk == tau) & (j >= 0) & (((uint32_t)j >> 5) == hi))
                 lds_inc(&sm.h2[(uint32_t)j & 31u]);
             });
-            ok = histogram_round<32, false, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, h);
+            ok = histogram_round<32, false, BS>(sm.h2, x + kXHist, round++, need, 0u, sy, sm,
+                                               h);
             cut.pos = (int32_t)((hi << 5) | h.bin);
           }
         }
