@@ -2,7 +2,7 @@
  * oracle_sanitize.c - drives the CPU oracle (oracle/topk_oracle.c) under
  * gcc's AddressSanitizer + UndefinedBehaviorSanitizer, or ThreadSanitizer.
  *
- * Test infrastructure: built and run by tests/test_oracle_sanitized.py on
+ * Test infrastructure: built and run by tests/test_sanitized.py on
  * the host only; it links the oracle's C file directly and nothing of the
  * GPU library.
  *
