@@ -12,18 +12,20 @@
 // Work decomposition, by the row's aligned span (seq_len plus the row
 // start's residue mod 4) and the batch's score stride (no span exceeds it):
 //   - trivial rows (seq_len <= k) write their positions and read no score;
-//   - register rows (span <= 32768): one workgroup per row loads the whole
-//     span once with 16-byte loads and keeps it in registers as keys; every
-//     later pass runs over registers (1024 threads per row for small
-//     batches of short strides, 256 threads up to a 16384 stride, 512
-//     threads for longer strides);
+//   - register rows: one workgroup per row loads the whole span once with
+//     16-byte loads and keeps it as keys, in registers and for the last
+//     slices of the longest ones in LDS (loaded there directly); every
+//     later pass runs over those. 1024 threads per row for small batches of
+//     short strides, 256 threads up to a 16384 stride, 512 threads up to
+//     40960-float spans for longer strides, and 1024-thread workgroups of
+//     the long-row kernel up to 65536;
 //   - long rows of batches with few of them (split rows): cut into
 //     segments of 4096 or 8192 floats, each held in registers by one
 //     workgroup of the register kernel; the segments merge their digit
 //     histograms through an exchange area in the plan buffer;
-//   - the other long rows: streamed once by a 1024-thread workgroup that
-//     keeps the pairs above a running threshold in LDS (a two-pass re-read
-//     serves the rare rows that defeat it).
+//   - the other long rows (span above 65536): streamed once by a
+//     1024-thread workgroup that keeps the pairs above a running threshold
+//     in LDS (a two-pass re-read serves the rare rows that defeat it).
 // The pages' CUDA design (register rows up to 8192 / 16384, a streaming
 // template, thread-block clusters for very long rows; PR #26788 and
 // PR #36684 digests) is prior art here: the widths and the capacities are
