@@ -15,7 +15,7 @@
 //   - register rows: one workgroup per row loads the whole span once with
 //     16-byte loads and keeps it as keys, in registers and for the last
 //     slices of the longest ones in LDS (loaded there directly); every
-//     later pass runs over those. 1024 threads per row for small batches of
+//     later pass runs over those. 512 threads per row for small batches of
 //     short strides, 256 threads up to a 16384 stride, 512 threads up to
 //     40960-float spans for longer strides, and 1024-thread workgroups of
 //     the long-row kernel up to 65536;
@@ -265,7 +265,7 @@ struct Emit {
 };
 
 // Shared memory of the register path.
-constexpr int kWideBlock = 1024;  // threads per row when rows are too few to fill the chip
+constexpr int kWideBlock = 512;  // threads per row when rows are too few to fill the chip
 static_assert(kMaxK + kBlock <= kBins, "a split segment's output stage and its dummies fit the histogram");
 
 template <int BS>
@@ -1992,9 +1992,12 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const Params p) {
   row_in_registers<kSmallVec>(row_view(p, b, r), p.k, em, sm);
 }
 
-// Same rows with 1024 threads per row (2 float4 per thread), for batches
+// Same rows with 512 threads per row (4 float4 per thread), for batches
 // too small to fill the chip: a row's latency, not the rows in flight,
-// sets the time.
+// sets the time. 512 threads put two waves of the row on each SIMD, where
+// 1024 put four that all run the searches' dependent steps (128 rows of
+// 8192 floats: 6.65 us per launch against 6.75 at 1024 threads and 8.1 at
+// 256; 4 rows of 3000: 6.0 us against 7.1 at 1024).
 template <bool kPaged>
 __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
   const int64_t b = blockIdx.x;
