@@ -331,6 +331,20 @@ def test_page_sizes(orc, page_size):
     check(orc, p, use_plan=False, with_raw=False)
 
 
+@pytest.mark.parametrize("page_size", [1, 2, 8, 16])
+def test_page_sizes_short_stride(orc, page_size):
+    """Rows in a score stride of 8192 with few rows (the rows of small
+    batches, 512 threads each): for an 8192-float window, page sizes 1, 2
+    and 8 need more table entries than the row's LDS copy holds, so the
+    emit reads the table from memory; 16 fills the copy exactly."""
+    rows = [(L, r, pat) for r in range(4) for L in (3000, 4097, 8192 - r)
+            for pat in ("normal", "alphabet")]
+    p = edge_batch(78, "paged", 1000, rows, page_size=page_size, name=f"short_pages_{page_size}",
+                   stride=8192)
+    assert p.stride == 8192 and p.num_rows <= 512
+    check(orc, p, use_plan=False, with_raw=True)
+
+
 def test_register_rows_are_byte_deterministic(orc):
     p = workloads.make_workload("paged_decode")
     d = gpu_run.to_dev(p)
