@@ -18,7 +18,8 @@
 //     later pass runs over those. 512 threads per row for small batches of
 //     short strides, 256 threads up to a 16384 stride, 512 threads up to
 //     40960-float spans for longer strides, and 1024-thread workgroups of
-//     the long-row kernel up to 65536;
+//     the long-row kernel up to 65536 (for a batch of 1024 rows or more
+//     whose stride is at most 65536, every row of it);
 //   - long rows of batches with few of them (split rows): cut into
 //     segments of 4096 or 8192 floats, each held in registers by one
 //     workgroup of the register kernel; the segments merge their digit
@@ -90,12 +91,15 @@ struct Params {
 
 // The long rows that are not split: with no plan, the streaming kernel
 // (one workgroup per row of the batch); with a plan of a batch of more than
-// kMaxSplitRows rows, the streaming kernel's persistent grid serves the
-// plan's streamed list and the register kernel, in pieces, any long row the
-// plan does not list (a plan built for other lengths); with a plan of a
-// smaller batch (every long row split), the register kernel, in pieces, any
-// long row the plan does not split.
-enum LongMode : int32_t { kLongPerRow = 0, kLongListed = 1, kLongInPieces = 2 };
+// kMaxSplitRows rows, the streaming kernel serves the plan's streamed list
+// (workgroup g its entry g) and the register kernel, in pieces, any long
+// row the plan does not list (a plan built for other lengths); with a plan
+// of a smaller batch (every long row split), the register kernel, in
+// pieces, any long row the plan does not split. kLongAll: a large batch
+// whose stride keeps every row in 1024 threads' registers (see
+// launch_rows): the long-row kernel alone serves every row, one
+// workgroup per row, and no row is split.
+enum LongMode : int32_t { kLongPerRow = 0, kLongListed = 1, kLongInPieces = 2, kLongAll = 3 };
 
 // Row classes by aligned span. A row's class is recomputed by every kernel
 // from the current seq_lens / row_starts; the plan only packs the rows of a
@@ -2853,8 +2857,15 @@ rows_long_kernel(const Params p) {
   int32_t s2 = __builtin_amdgcn_readfirstlane(ld_const(a_s2));
   const RowMeta m = row_meta<kPaged>(p, b, true);
   asm volatile("" : "+s"(l2), "+s"(s2));
-  if (m.r.cls != kClassLong || m.split) return;
-  if (p.long_mode == kLongListed && !m.streamed) return;
+  if (p.long_mode == kLongAll) {
+    if (m.r.L <= p.k) {
+      write_trivial<kPaged, kLongBlock>(row_emit<kPaged>(p, b, m), m.r.L, p.k);
+      return;
+    }
+  } else {
+    if (m.r.cls != kClassLong || m.split) return;
+    if (p.long_mode == kLongListed && !m.streamed) return;
+  }
   Prefetch pf{nullptr, 0};
   if (t2) {
     const RowInfo r2 = classify(l2, p.row_starts ? s2 : 0, p.k);
@@ -3023,6 +3034,17 @@ int check_common(const float* scores, int64_t score_stride, const int32_t* seq_l
 // than about two per CU, per-row latency sets the time.
 constexpr int32_t kWideRows = 512;
 
+// From this many rows, a batch whose stride admits long rows but no row
+// beyond 1024 threads' registers (40961 .. 65536 floats) runs in the
+// long-row kernel alone, every row in one workgroup. The register kernel's
+// launch would otherwise cost one workgroup per row even where the long
+// rows are all of the batch (13 us of 235 at 5462 rows of 49152 floats;
+// the long rows took 223). Rows of 40960 floats and less then run at 1024
+// threads instead of 512, and long rows are not split: a smaller batch
+// (few long rows among many short ones: 300 rows at 20 us split, 29 us
+// whole) keeps the split path.
+constexpr int32_t kLongAllRows = 1024;
+
 struct KernelLaunch {
   void (*fn)(Params);
   dim3 grid;
@@ -3032,11 +3054,12 @@ struct KernelLaunch {
 // The kernels for a batch, in stream order, chosen by the score stride (a
 // row's span never exceeds it). Up to 8192 floats every row is short: the
 // short-row kernel (or the wide one, for few rows) serves the batch alone;
-// up to 16384 the mid kernel alone; up to 32768 the register kernel alone.
-// Longer strides: the register kernel, whose first workgroups are the split
-// workers when a plan is given, then the streaming kernel, unless the plan
-// splits every long row (at most kMaxSplitRows rows). Each launch reports
-// its own status.
+// up to 16384 the mid kernel alone; up to 40960 the register kernel alone;
+// up to 65536, from kLongAllRows rows, the long-row kernel alone (the plan
+// is not used). Other strides: the register kernel, whose first
+// workgroups are the split workers when a plan is given, then the
+// streaming kernel, unless the plan splits every long row (at most
+// kMaxSplitRows rows). Each launch reports its own status.
 template <bool kPaged>
 int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
@@ -3054,6 +3077,10 @@ int launch_rows(Params p, hipStream_t stream) {
       ls[n++] = {rows_short_kernel<kPaged>, grid, dim3(kBlock)};
   } else if (p.stride <= (int64_t)kLargeVec * 4 * kBlock) {
     ls[n++] = {rows_mid_kernel<kPaged>, grid, dim3(kBlock)};
+  } else if (lng && p.stride <= (int64_t)kLongRegCap && p.num_rows >= kLongAllRows) {
+    p.plan = nullptr;
+    p.long_mode = kLongAll;
+    ls[n++] = {rows_long_kernel<kPaged>, grid, dim3(kLongBlock)};
   } else {
     if (p.plan) {
       const int64_t w = plan_split_cap(p.num_rows) * kMaxSeg;

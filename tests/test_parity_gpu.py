@@ -158,6 +158,40 @@ def test_band_edges(orc, band, k, mode):
     check(orc, p, use_plan=False, with_raw=(mode == "paged"))
 
 
+def _long_all_rows(k, stride=65536):
+    """Every start residue; lengths -3, 0, 1, k-1, k, k+1, 12000, the spans
+    around 40960 and 49152 and the four spans below the stride; every value
+    pattern and tie classes of at most 64 and more than 64 elements."""
+    rows = []
+    for r in range(4):
+        top = [stride - r - d for d in range(4)]
+        for L in (-3, 0, 1, k - 1, k, k + 1, 12000, 40959 - r, 40960 - r, 40961 - r,
+                  49152 - r, *top):
+            rows.append((L, r, "normal"))
+        for pat in PATTERNS:
+            for L in (3000, 45000 - r, stride - r):
+                rows.append((L, r, pat))
+        for L in (3000, stride - r):
+            for tied, need in ((64, 1), (64, 37), (65, 40), (2, 1), (200, 150)):
+                if need <= k and k - need + tied <= L:
+                    rows.append((L, r, ("ties", k - need, tied)))
+    return rows
+
+
+@pytest.mark.parametrize("mode,k,use_plan", [("paged", 2048, True), ("paged", 7, False),
+                                             ("ragged", 2048, False), ("ragged", 1, True)])
+def test_long_kernel_serves_every_row(orc, mode, k, use_plan):
+    """A batch of 1024 rows or more at a score stride of 65536 floats: the
+    long-row kernel alone serves every row (trivial, short, register-length
+    and long, up to the stride), with every start residue, the value
+    patterns and tie classes; a plan, when given, is not used."""
+    rows = _long_all_rows(k)
+    rows = rows * (1024 // len(rows) + 1)
+    p = edge_batch(6000 + k, mode, k, rows, stride=65536, name=f"long_all_{mode}_k{k}")
+    assert p.stride == 65536 and p.num_rows >= 1024
+    check(orc, p, use_plan=use_plan, with_raw=(mode == "paged"))
+
+
 def test_all_trivial_rows(orc):
     """Every row's window fits in k: the trivial path alone, compared with
     the oracle (the counter run shows that it reads no scores)."""
