@@ -56,11 +56,13 @@ constexpr int kBigCap = (kBigVec + kBigLds) * 4 * kBigBlock;  // 40960
 constexpr int kStreamVec = 8;         // float4 per thread per streaming chunk
 constexpr int kStreamCandCap = 2048;  // streaming path: threshold-bin pairs in LDS
 constexpr int kPtCap = 512;           // page-table entries staged in LDS
-// 1024-thread rows stage more (their LDS has room): the tables of register
-// rows up to 131072 floats at a page size of 64
+// 1024-thread rows stage more (their LDS has room): one entry per thread,
+// the table of a register row of 65536 floats at a page size of 64 (a
+// second entry per thread took a VGPR that the long rows' registers need:
+// one spilled register, reloaded in every row's cut)
 template <int BS>
 constexpr int pt_cap() {
-  return BS >= 1024 ? 2048 : kPtCap;
+  return BS >= 1024 ? 1024 : kPtCap;
 }
 
 struct Params {
