@@ -274,9 +274,11 @@ struct Emit {
 constexpr int kWideBlock = 512;  // threads per row when rows are too few to fill the chip
 static_assert(kMaxK + kBlock <= kBins, "a split segment's output stage and its dummies fit the histogram");
 
-template <int BS>
+// NB: bins of the first key digit (4096, or 16384 for the rows of the
+// latency-bound wide kernel, whose first digit then takes 14 key bits).
+template <int BS, int NB = kBins>
 struct SmemRegB {
-  uint32_t hist[kBins];        // every histogram of the row's digits; finally the output stage
+  uint32_t hist[NB];           // every histogram of the row's digits; finally the output stage
   int32_t pt[pt_cap<BS>()];    // the row's page-table entries (PAGED)
   uint32_t wave_cnt[BS / 64];  // per wave: selected elements
   uint32_t bcast[4];           // a bin search's result, when one wave searches
@@ -632,11 +634,19 @@ __device__ __forceinline__ BinHit all_waves_find(const uint32_t* hist, uint32_t 
   auto bin_of = [](int r) { return kDesc ? NB - 1 - r : r; };  // scan position -> bin
   uint32_t sum = 0;
   {
+    // Runs of 32 bins and more are 128 bytes apart or more: read in step,
+    // every lane's chunk would sit on the same LDS banks, so each lane
+    // starts at another 16-byte chunk of its run (the sum does not care
+    // about the order). Shorter runs read in step: there the rotation's
+    // address arithmetic cost more than the conflicts (mid-kernel rows
+    // 4.5% slower with it).
+    constexpr int CH = PER / 4;
     const int lo = kDesc ? NB - (u + 1) * PER : u * PER;
     const uint4* h4 = reinterpret_cast<const uint4*>(hist + lo);
+    const int rot = CH >= 8 ? (lane & (CH - 1)) : 0;
 #pragma unroll
-    for (int i = 0; i < PER / 4; ++i) {
-      const uint4 q = h4[i];
+    for (int i = 0; i < CH; ++i) {
+      const uint4 q = h4[CH >= 8 ? ((i + rot) & (CH - 1)) : i];
       sum += q.x + q.y + q.z + q.w;
     }
   }
@@ -677,8 +687,8 @@ template <class Sm>
 struct HasWaveSums {
   static constexpr bool value = false;
 };
-template <int BS>
-struct HasWaveSums<SmemRegB<BS>> {
+template <int BS, int NB>
+struct HasWaveSums<SmemRegB<BS, NB>> {
   static constexpr bool value = BS >= kBlock;
 };
 template <int BS>
@@ -751,12 +761,12 @@ struct SparseBin<Src, decltype(void(Src::kPerThread))> {
 // key (low8_zero). Each level costs one filtered pass over the registers
 // and a search. Ties at the k-th key: a class of at most 64 elements is
 // ranked by position in one pass; a larger one takes two position digits.
+// refine_from_level1 takes the level-1 search's result h (need = k minus
+// h.before elements still to take from bin h.bin), with sm.tie_n zeroed
+// behind that search's barrier.
 template <int BS, class Src, class Sm>
-__device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint32_t k,
-                                                   bool low8_zero = false) {
-  if (tix() == 0) sm.tie_n = 0u;  // the first search's barrier publishes it
-  BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
-  uint32_t need = k - h.before;
+__device__ __forceinline__ Cut refine_from_level1(const Src& src, Sm& sm, BinHit h, uint32_t need,
+                                                  bool low8_zero = false) {
   uint32_t prefix = h.bin;  // key bits 31..20
   if (h.cnt == need) return Cut{20, prefix, kAllPos};
   // every wave is past the search's barrier: the level-1 counts are dead
@@ -826,6 +836,14 @@ __device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint3
   __syncthreads();
   h = group_find<32, false, BS>(sm.hist, need, sm);
   return Cut{0, tau, (int32_t)((hi << 5) | h.bin)};
+}
+
+template <int BS, class Src, class Sm>
+__device__ __forceinline__ Cut refine_in_registers(const Src& src, Sm& sm, uint32_t k,
+                                                   bool low8_zero = false) {
+  if (tix() == 0) sm.tie_n = 0u;  // the first search's barrier publishes it
+  const BinHit h = group_find<kBins, true, BS>(sm.hist, k, sm);
+  return refine_from_level1<BS>(src, sm, h, k - h.before, low8_zero);
 }
 
 // Whole span in registers (span <= NV * 4 * BS).
@@ -969,6 +987,96 @@ __device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
   return tot;
 }
 
+// The elements of the k-th key's first-digit bin are ranked directly when
+// there are at most this many of them (a pair compare per element pair).
+constexpr uint32_t kRankCap = 256;
+
+// Stage the k selected positions of a register row when the k-th largest
+// key lies in the first-digit bin [lo, hi] with `before` keys above it and
+// `need` of its elements to take. One pass counts, per thread, the keys
+// above hi (taken) and the window keys in the bin (candidates); a second
+// writes the taken positions to stage[0 .. before) and the candidates to
+// LDS as 64-bit (key, ~position) words, whose order is the selection
+// order (higher key, then lower position). A candidate's rank is the
+// number of candidates with a larger word (1 to 4 lanes share one
+// candidate's compares); ranks below need take stage slot before + rank.
+// Key 0 (columns outside the window) is never a candidate. The caller's
+// search has closed with a barrier (the histogram is free).
+template <int BS, class Src, class Sm>
+__device__ __forceinline__ void stage_by_rank(const Src& src, uint32_t lo, uint32_t hi,
+                                              uint32_t before, uint32_t need, int32_t* stage,
+                                              Sm& sm) {
+  constexpr int W = BS / 64;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const uint32_t clo = lo ? lo : 1u;
+  // per lane: keys above hi; per wave (scalar): candidates
+  uint32_t n_win = 0;
+  uint32_t c_wave = 0;
+  src.for_each([&](uint32_t kk, int32_t) {
+    const uint64_t m_win = __ballot(kk > hi);
+    n_win = add_lane_bit(n_win, m_win);
+    c_wave += (uint32_t)__builtin_popcountll(__ballot(kk >= clo) & ~m_win);
+  });
+  const uint32_t iw = wave_inclusive_sum(n_win);
+  // one word per wave: winners (below k <= 2048) in the low half,
+  // candidates (at most kRankCap) in the high half
+  if (lane == 63) sm.wave_cnt[w] = iw | (c_wave << 16);
+  __syncthreads();
+  uint32_t sw = iw - n_win;
+  uint32_t sc;
+  uint32_t n;
+  {
+    const uint32_t a = lane < W ? sm.wave_cnt[lane] : 0u;
+    const uint32_t ia = wave_inclusive_sum(a);
+    const uint32_t pre = w ? read_lane(ia, w - 1) : 0u;
+    sw += pre & 0xffffu;
+    sc = pre >> 16;
+    n = read_lane(ia, W - 1) >> 16;
+  }
+  uint64_t* cand = reinterpret_cast<uint64_t*>(stage + kMaxK);
+  // zero words after the last candidate: the rank loop reads in groups
+  // of four (a zero word is below every candidate's)
+  if (tix() < 16) cand[n + tix()] = 0ull;
+  // a lane whose element is not taken writes its own spare word instead
+  // of branching around the store
+  const int32_t spare = kMaxK + 2 * ((int32_t)kRankCap + 16) + lane;
+  src.for_each([&](uint32_t kk, int32_t j) {
+    const bool win = kk > hi;
+    const uint64_t m_win = __ballot(win);
+    stage[win ? (int32_t)sw : spare] = j;
+    sw = add_lane_bit(sw, m_win);
+    const uint64_t m_c = __ballot(kk >= clo) & ~m_win;
+    if (m_c) {
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_c >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m_c, 0u));
+      if ((kk >= clo) & !win) cand[sc + r] = ((uint64_t)kk << 32) | (uint32_t)~j;
+      sc += (uint32_t)__builtin_popcountll(m_c);
+    }
+  });
+  __syncthreads();
+  const uint32_t lg = n * 4 <= (uint32_t)BS ? 2u : n * 2 <= (uint32_t)BS ? 1u : 0u;
+  const uint32_t g = 1u << lg;
+  const uint32_t t = (uint32_t)tix();
+  const uint32_t i = t >> lg;
+  const uint32_t part = t & (g - 1u);
+  uint32_t r = 0;
+  uint64_t mine = 0;
+  if (i < n) {
+    mine = cand[i];
+    // four reads in flight per step
+    for (uint32_t q = part; q < n; q += 4 * g) {
+      const uint64_t c0 = cand[q], c1 = cand[q + g], c2 = cand[q + 2 * g], c3 = cand[q + 3 * g];
+      r += (c0 > mine ? 1u : 0u) + (c1 > mine ? 1u : 0u) + (c2 > mine ? 1u : 0u) +
+           (c3 > mine ? 1u : 0u);
+    }
+  }
+  // a candidate's lanes are adjacent: sum them within pairs, then quads
+  if (lg >= 1) r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xb1, 0xf, 0xf, false);
+  if (lg >= 2) r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4e, 0xf, 0xf, false);
+  if (i < n && part == 0 && r < need) stage[before + r] = (int32_t)~(uint32_t)mine;
+}
+
 // The cut of a register row whose level-1 histogram is in sm.hist, then
 // the stage and the emit. The selected positions go to LDS (the
 // histogram's space, free after the cut), then one coalesced pass maps and
@@ -977,11 +1085,46 @@ __device__ __forceinline__ uint32_t count_at_least(const Src& src, uint32_t thr,
 // elements. With one (several elements hold exactly the k-th key tau and
 // only those at positions <= pos are taken) the rare second form applies,
 // with a guard on the slot.
-template <bool kPaged, int BS, int kPolicy, class Src>
+template <bool kPaged, int BS, int kPolicy, class Src, int NB>
 __device__ __forceinline__ void cut_stage_emit(const Src& src, const Emit<kPaged>& em, int32_t L,
-                                               int32_t k, SmemRegB<BS>& sm) {
-  const Cut cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
+                                               int32_t k, SmemRegB<BS, NB>& sm) {
   int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  Cut cut;
+  if constexpr (NB == kBins) {
+    cut = refine_in_registers<BS>(src, sm, (uint32_t)k);
+  } else {
+    // A 14-bit first digit (bits 31..18): its threshold bin holds about a
+    // quarter of a 12-bit one's elements, so that for most rows the bin's
+    // elements are ranked directly instead of taking a second digit.
+    static_assert(NB == 4 * kBins, "a 14-bit first digit");
+    constexpr uint32_t kShift = 18;
+    if (tix() == 0) sm.tie_n = 0u;  // the search's barrier publishes it
+    const BinHit h = group_find<NB, true, BS>(sm.hist, (uint32_t)k, sm);
+    const uint32_t need = (uint32_t)k - h.before;
+    if (h.cnt == need) {
+      cut = Cut{kShift, h.bin, kAllPos};
+    } else if (h.cnt <= kRankCap) {
+      stage_by_rank<BS>(src, h.bin << kShift, (h.bin << kShift) | ((1u << kShift) - 1u),
+                        h.before, need, stage, sm);
+      __syncthreads();
+      write_stage<kPaged, BS, kPolicy>(em, stage, L, k, sm.pt);
+      return;
+    } else {
+      // Too many for ranking: the 12-bit digit's result from the four
+      // 14-bit bins of its bin, then the 12-bit refinement.
+      const uint32_t b12 = h.bin >> 2;
+      uint32_t cnt12 = 0, above = 0;
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t c = sm.hist[4 * b12 + q];
+        cnt12 += c;
+        above += 4 * b12 + q > h.bin ? c : 0u;
+      }
+      const BinHit h12{b12, h.before - above, cnt12};
+      __syncthreads();  // the counts are read before the refinement clears them
+      cut = refine_from_level1<BS>(src, sm, h12, (uint32_t)k - h12.before);
+    }
+  }
   if (cut.pos == kAllPos) {
     const uint32_t lo = cut.prefix << cut.shift;
     const uint32_t thr = lo ? lo : 1u;
@@ -1003,11 +1146,13 @@ __device__ __forceinline__ void cut_stage_emit(const Src& src, const Emit<kPaged
 
 // The rest of the register path, once the row's vectors are in x (and the
 // caller has staged the page table, if it stages it).
-template <int NV, bool kPaged, int BS>
+template <int NV, bool kPaged, int BS, int NB>
 __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4 (&x)[NV],
                                                  const int32_t (&tv)[table_per_thread<BS>()],
                                                  int32_t k, Emit<kPaged> em,
-                                                 SmemRegB<BS>& sm) {
+                                                 SmemRegB<BS, NB>& sm) {
+  // first digit: the top 12 (or 14) key bits
+  constexpr uint32_t kShift1 = NB == kBins ? 20 : 18;
   const int32_t t = tix();
   const int32_t L = rv.span - rv.rem;
   // Register slices 0 .. ilast hold the span's vectors; later slices hold
@@ -1015,7 +1160,7 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
   const int32_t ilast = __builtin_amdgcn_readfirstlane((((rv.span + 3) >> 2) - 1) / BS);
   uint32_t key[NV][4];
   if constexpr (BS <= kBlock) store_table<kPaged, BS>(em, sm.pt, L, tv);
-  clear_bins<kBins, BS>(sm.hist);
+  clear_bins<NB, BS>(sm.hist);
   __syncthreads();
   // Slice by slice as its loads land: keys, then the level-1 histogram.
   // Columns outside the window get key 0, below every float's key except
@@ -1043,7 +1188,7 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
             if (a + c >= rv.span) key[i][c] = 0u;
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> 20], one);
+        for (int c = 0; c < 4; ++c) lds_add(&sm.hist[key[i][c] >> kShift1], one);
       }
     }
   }
@@ -1058,9 +1203,9 @@ __device__ __forceinline__ void row_from_vectors(const RowView& rv, const float4
       src, em, L, k, sm);
 }
 
-template <int NV, bool kPaged, int BS = kBlock>
+template <int NV, bool kPaged, int BS = kBlock, int NB = kBins>
 __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, Emit<kPaged> em,
-                                                 SmemRegB<BS>& sm) {
+                                                 SmemRegB<BS, NB>& sm) {
   // Nothing of this row is in flight: this wait costs nothing and keeps the
   // compiler from draining the table load before the score loads (a load
   // another path leaves pending into a register it reuses here).
@@ -1069,7 +1214,7 @@ __device__ __forceinline__ void row_in_registers(const RowView& rv, int32_t k, E
   load_table<kPaged, BS>(em, rv.span - rv.rem, tv);
   float4 x[NV];
   load_row<NV, BS>(rv, x);
-  row_from_vectors<NV, kPaged, BS>(rv, x, tv, k, em, sm);
+  row_from_vectors<NV, kPaged, BS, NB>(rv, x, tv, k, em, sm);
 }
 
 // Rows longer than the registers hold: NL more slices of the row, loaded
@@ -2031,6 +2176,11 @@ __global__ __launch_bounds__(kBlock) void rows_short_kernel(const Params p) {
 // 1024 put four that all run the searches' dependent steps (128 rows of
 // 8192 floats: 6.65 us per launch against 6.75 at 1024 threads and 8.1 at
 // 256; 4 rows of 3000: 6.0 us against 7.1 at 1024).
+// The first key digit takes 14 bits (a 64 KiB histogram: one workgroup per
+// CU at these batch sizes has the LDS): its threshold bin holds about 40 of
+// a decode row's 8192 keys, which are ranked directly instead of taking a
+// second 12-bit digit and a separate stage pass (128 rows of 8192 floats:
+// 6.60 -> 6.17 us per launch; 4 rows of 3000: 6.00 -> 5.90 us).
 template <bool kPaged>
 __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
   const int64_t b = blockIdx.x;
@@ -2042,9 +2192,9 @@ __global__ __launch_bounds__(kWideBlock) void rows_wide_kernel(const Params p) {
     write_trivial<kPaged, kWideBlock>(em, r.L, p.k);
     return;
   }
-  __shared__ SmemRegB<kWideBlock> sm;
-  row_in_registers<kSmallVec * kBlock / kWideBlock, kPaged, kWideBlock>(row_view(p, b, r), p.k,
-                                                                         em, sm);
+  __shared__ SmemRegB<kWideBlock, 4 * kBins> sm;
+  row_in_registers<kSmallVec * kBlock / kWideBlock, kPaged, kWideBlock, 4 * kBins>(
+      row_view(p, b, r), p.k, em, sm);
 }
 
 // Every row of a batch with a score stride of 8193 .. 16384 floats, in one

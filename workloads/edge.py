@@ -11,7 +11,7 @@ import numpy as np
 from .configs import OUTSIDE_SCORE, PAGE_SIZE, Problem, random_page_tables
 
 PATTERNS = ("normal", "fp16", "alphabet", "equal", "neg_inf", "increasing", "decreasing",
-            "zeros_mixed", "one_pos_inf", "rising_head")
+            "zeros_mixed", "one_pos_inf", "rising_head", "dense")
 
 _ALPHABET = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.0, np.inf], dtype=np.float32)
 
@@ -59,6 +59,12 @@ def _values(rng, pattern, L: int) -> np.ndarray:
         v = np.float32(-2.0) + np.float32(0.1) * rng.standard_normal(L, dtype=np.float32)
         v[:h] = np.linspace(-3.0, 3.0, h, dtype=np.float32)
         return v
+    if pattern == "dense":
+        # every value in [0.75, 0.8125): one bin of the top 12 key bits,
+        # spread over its four 14-bit sub-bins, so the k-th key's fine bin
+        # holds hundreds of elements with others above it in the same
+        # coarse bin
+        return rng.uniform(0.75, 0.8125, size=L).astype(np.float32)
     if pattern == "one_pos_inf":
         v = np.full(L, -np.inf, dtype=np.float32)
         v[rng.integers(0, L)] = np.inf
