@@ -162,13 +162,14 @@ constexpr int kCandCapG = 2048;  // threshold-bin elements resolved by the last 
 // the round word should not queue behind the arrivals.
 enum XWord : int32_t {
   kXHist = 0,       // 4096 bins: the current digit round's merged histogram
-  kXCand = 4096,    // kCandCapG (key, position) pairs of the level-1 bin
-  kXFlag = 8192,    // 64-bit: last published round and its result
-  kXArrive = 8224,  // segments arrived (all rounds)
-  kXOut = 8288,     // 64-bit: output slots taken (low), candidate pairs written (high)
-  kXDone = 8320,    // segments finished
-  kXFail = 8352,    // a segment of the row gave up waiting
-  kXWords = 8384,   // multiple of 64 words (256 bytes)
+  kXCand = 4096,     // kCandCapG (key, position) pairs of the level-1 bin
+  kXVal = 8192,      // their emitted values (page-mapped or offset), pair for pair
+  kXFlag = 10240,    // 64-bit: last published round and its result
+  kXArrive = 10272,  // segments arrived (all rounds)
+  kXOut = 10336,     // 64-bit: output slots taken (low), candidate pairs written (high)
+  kXDone = 10368,    // segments finished
+  kXFail = 10400,    // a segment of the row gave up waiting
+  kXWords = 10432,   // multiple of 64 words (256 bytes)
 };
 
 __host__ __device__ constexpr int64_t plan_split_cap(int64_t rows) {
@@ -2347,8 +2348,20 @@ __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_
   const bool last = sy.arrive(round);
   uint64_t mine = 0;
   if (last) {
-    for (int32_t i = t; i < NB; i += BS)
-      lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (NB % (4 * BS) == 0) {
+      // 16 bytes per load, with the cache policy of a relaxed device-scope
+      // atomic load (sc1): the totals as the other segments' atomics left them
+      const __amdgpu_buffer_rsrc_t rh = words_buffer(reinterpret_cast<int32_t*>(g_hist), NB);
+#pragma unroll
+      for (int q = 0; q < NB / (4 * BS); ++q) {
+        const int32_t i4 = q * BS + t;
+        reinterpret_cast<uint4*>(lds_hist)[i4] =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, i4 * 16, 0, 16));
+      }
+    } else {
+      for (int32_t i = t; i < NB; i += BS)
+        lds_hist[i] = __hip_atomic_load(&g_hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     // (4096 bins: every wave searches a part; fewer: one wave each)
     const BinHit f = group_find<NB, kDesc, BS>(lds_hist, need, sm);
@@ -2369,61 +2382,89 @@ __device__ __forceinline__ bool histogram_round(uint32_t* lds_hist, uint32_t* g_
   return ok;
 }
 
-// The exact cut among n (key, position) pairs in LDS, all inside one
-// level-1 bin, taking `need` of them; the whole workgroup. The keys' AND
-// and OR give the bits in which they differ: 8-bit digit rounds run over
-// those bits only (the bits below them are the same in every key), each a
-// histogram of the candidates still matching the digits fixed so far.
-// Ties at the k-th key take the lowest positions: a tie class of at most 64
-// elements is gathered and ranked on lane masks, a larger one takes
-// position digits (8, 8 and 1 bits). The result selects key > tau, or
-// key == tau at position <= pos (pos == kAllPos: every such key).
-template <int BS>
-__device__ __forceinline__ Cut resolve_pairs_group(const uint2* cand, uint32_t n, uint32_t need,
-                                                   SmemSplitB<BS>& sm) {
+// AND / OR of v over the wave, in lane 63 (DPP row shifts, then the row
+// broadcasts; a lane with no source keeps its own value).
+__device__ __forceinline__ uint32_t wave_and63(uint32_t v) {
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xf, 0xf, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xf, 0xf, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xf, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xf, 0xf, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or63(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+// The exact cut among the candidate (key, position) pairs of one level-1
+// bin, NP per thread in registers (key 0: no candidate), taking `need` of
+// them; the whole workgroup. The keys' AND and OR give the bits in which
+// they differ: 8-bit digit rounds run over those bits only (the bits below
+// them are the same in every key), each a histogram of the candidates
+// still matching the digits fixed so far, searched by every wave. Ties at
+// the k-th key take the lowest positions: a tie class of at most 64
+// elements is gathered and ranked on lane masks by wave 0, a larger one
+// takes position digits (8, 8 and 1 bits). The result selects key > tau,
+// or key == tau at position <= pos (pos == kAllPos: every such key).
+template <int BS, int NP>
+__device__ __forceinline__ Cut resolve_pairs_regs(const uint32_t (&ck)[NP], const int32_t (&cp)[NP],
+                                                  uint32_t n, uint32_t need, SmemSplitB<BS>& sm) {
   const int32_t t = tix();
+  const int lane = lane_id();
   uint32_t a = 0xffffffffu, o = 0u;
-  for (uint32_t i = (uint32_t)t; i < n; i += BS) {
-    const uint32_t kk = cand[i].x;
-    a &= kk;
-    o |= kk;
-  }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    a &= (uint32_t)__shfl_xor((int)a, d);
-    o |= (uint32_t)__shfl_xor((int)o, d);
+  for (int q = 0; q < NP; ++q) {
+    if (ck[q]) {
+      a &= ck[q];
+      o |= ck[q];
+    }
   }
+  a = wave_and63(a);
+  o = wave_or63(o);
   if (t == 0) {
     sm.bcast[0] = 0xffffffffu;
     sm.bcast[1] = 0u;
     sm.tie_n = 0u;
   }
+  if (t < 256) sm.h2[t] = 0u;  // the first digit round's histogram
   __syncthreads();
-  if (lane_id() == 0) {
+  if (lane == 63) {
     atomicAnd(&sm.bcast[0], a);
     atomicOr(&sm.bcast[1], o);
   }
   __syncthreads();
   const uint32_t all_and = __builtin_amdgcn_readfirstlane(sm.bcast[0]);
   const uint32_t diff = all_and ^ __builtin_amdgcn_readfirstlane(sm.bcast[1]);
-  __syncthreads();  // the searches below broadcast through bcast
   uint32_t fixed = all_and & ~diff;  // the key bits decided so far
   uint32_t cnt = n;
   if (diff) {
     const int lo_bit = __builtin_ctz(diff);
+    bool first = true;
     for (int top = 31 - __builtin_clz(diff); top >= lo_bit; top -= 8) {
       const int width = top - lo_bit + 1 < 8 ? top - lo_bit + 1 : 8;
       const int sh = top - width + 1;
       const uint32_t above = top == 31 ? 0u : fixed >> (top + 1);
-      if (t < 256) sm.h2[t] = 0u;
-      __syncthreads();
-      for (uint32_t i = (uint32_t)t; i < n; i += BS) {
-        const uint32_t kk = cand[i].x;
-        if (top == 31 || (kk >> (top + 1)) == above)
+      if (!first) {
+        __syncthreads();  // every wave's search of the last round is done
+        if (t < 256) sm.h2[t] = 0u;
+        __syncthreads();
+      }
+      first = false;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const uint32_t kk = ck[q];
+        if ((kk != 0u) & ((top == 31) | ((kk >> (top + 1)) == above)))
           lds_inc(&sm.h2[(kk >> sh) & ((1u << width) - 1u)]);
       }
       __syncthreads();
-      const BinHit b = wave0_find<256, true>(sm.h2, need, sm);
+      const BinHit b = wave_find<256, true>(sm.h2, need);
       need -= b.before;
       fixed |= b.bin << sh;
       cnt = b.cnt;
@@ -2435,31 +2476,33 @@ __device__ __forceinline__ Cut resolve_pairs_group(const uint2* cand, uint32_t n
   }
   const uint32_t tau = fixed;  // every key bit decided: the tied key
   if (cnt <= 64u) {
-    for (uint32_t i = (uint32_t)t; i < n; i += BS) {
-      const uint2 e = cand[i];
-      if (e.x == tau) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      if ((ck[q] == tau) & (ck[q] != 0u)) {
         const uint32_t slot = atomicAdd(&sm.tie_n, 1u);
-        if (slot < 64u) sm.tie[slot] = e.y;
+        if (slot < 64u) sm.tie[slot] = (uint32_t)cp[q];
       }
     }
     __syncthreads();
-    const int lane = lane_id();
-    const uint32_t p = lane < (int)cnt ? sm.tie[lane] : 0u;
-    uint64_t live = cnt >= 64u ? ~0ull : (1ull << cnt) - 1ull;
+    if (wave_id() == 0) {
+      const uint32_t p = lane < (int)cnt ? sm.tie[lane] : 0u;
+      uint64_t live = cnt >= 64u ? ~0ull : (1ull << cnt) - 1ull;
 #pragma unroll
-    for (int b = 16; b >= 0; --b) {
-      const uint64_t zeros = __ballot(((p >> b) & 1u) == 0u) & live;
-      const uint32_t c0 = (uint32_t)__builtin_popcountll(zeros);
-      if (need <= c0) {
-        live = zeros;
-      } else {
-        need -= c0;
-        live &= ~zeros;
+      for (int b = 16; b >= 0; --b) {
+        const uint64_t zeros = __ballot(((p >> b) & 1u) == 0u) & live;
+        const uint32_t c0 = (uint32_t)__builtin_popcountll(zeros);
+        if (need <= c0) {
+          live = zeros;
+        } else {
+          need -= c0;
+          live &= ~zeros;
+        }
       }
+      const uint32_t pos = read_lane(p, live ? __builtin_ctzll(live) : 0);
+      if (lane == 0) sm.bcast[2] = pos;
     }
-    const uint32_t pos = read_lane(p, live ? __builtin_ctzll(live) : 0);
-    __syncthreads();  // tie and tie_n may be reused by the caller
-    return Cut{0, tau, (int32_t)pos};
+    __syncthreads();
+    return Cut{0, tau, (int32_t)__builtin_amdgcn_readfirstlane(sm.bcast[2])};
   }
   // a large tie class: position digits 16..9, 8..1, 0
   uint32_t pprefix = 0;
@@ -2468,15 +2511,17 @@ __device__ __forceinline__ Cut resolve_pairs_group(const uint2* cand, uint32_t n
   for (int d = 0; d < 3; ++d) {
     const int sh = pos_shift[d];
     const int wd = pos_width[d];
+    __syncthreads();  // the last search's reads of h2 are done
     if (t < 256) sm.h2[t] = 0u;
     __syncthreads();
-    for (uint32_t i = (uint32_t)t; i < n; i += BS) {
-      const uint2 e = cand[i];
-      if ((e.x == tau) & ((e.y >> (sh + wd)) == pprefix))
-        lds_inc(&sm.h2[(e.y >> sh) & ((1u << wd) - 1u)]);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const uint32_t j = (uint32_t)cp[q];
+      if ((ck[q] == tau) & (ck[q] != 0u) & ((j >> (sh + wd)) == pprefix))
+        lds_inc(&sm.h2[(j >> sh) & ((1u << wd) - 1u)]);
     }
     __syncthreads();
-    const BinHit b = wave0_find<256, false>(sm.h2, need, sm);
+    const BinHit b = wave_find<256, false>(sm.h2, need);
     need -= b.before;
     pprefix = (pprefix << wd) | b.bin;
   }
@@ -2584,12 +2629,22 @@ __device__ __forceinline__ void split_emit_cands(const Src& src, uint32_t T,
   const uint32_t base = __builtin_amdgcn_readfirstlane(sm.word[5]);
   at += __builtin_amdgcn_readfirstlane(sm.word[6]);
   uint64_t* gcand = reinterpret_cast<uint64_t*>(x + kXCand);
+  // a candidate's emitted value goes with it, so the row's last segment
+  // reads it with the pair instead of looking it up after the pair
+  auto cand_value = [&](int32_t j) -> int32_t {
+    if ((uint32_t)j >= (uint32_t)L) return -1;
+    if constexpr (kPaged) return em.staged ? em.value_lds(j, sm.pt) : em.value(j);
+    else return em.value(j);
+  };
   src.for_each([&](uint32_t kk, int32_t j) {
     const bool s = cand(kk);
     const uint64_t m = __ballot(s);
-    if (s & (at < (uint32_t)kCandCapG))
+    if (s & (at < (uint32_t)kCandCapG)) {
       __hip_atomic_store(&gcand[at], ((uint64_t)(uint32_t)j << 32) | kk, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&x[kXVal + at], (uint32_t)cand_value(j), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
     at = add_lane_bit(at, m);
   });
   auto put = [&](auto value) {
@@ -2721,21 +2776,25 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
         // the last segment: every candidate is in; resolve and emit them
         const uint32_t n = h.cnt;
         const uint64_t* gcand = reinterpret_cast<const uint64_t*>(x + kXCand);
-        uint2* lcand = reinterpret_cast<uint2*>(sm.hist);  // kCandCapG pairs fill the histogram
-        // Each thread's candidates (i = t + s BS) and their emitted values:
-        // the page-table lookups are issued now and land during the resolve.
+        // Each thread's candidates (i = t + q BS) and their emitted values
+        // in registers (the values' loads land during the resolve).
         constexpr int kCandPer = kCandCapG / BS;
+        uint32_t ck[kCandPer];
+        int32_t cp[kCandPer];
         int32_t cval[kCandPer];
 #pragma unroll
         for (int q = 0; q < kCandPer; ++q) {
           const uint32_t i = (uint32_t)(q * BS + t);
+          ck[q] = 0u;
+          cp[q] = -1;
           cval[q] = 0;
           if (i < n) {
             const uint64_t e =
                 __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            lcand[i] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
-            const int32_t j = (int32_t)(e >> 32);
-            if ((uint32_t)j < (uint32_t)r.L) cval[q] = em.value(j);
+            ck[q] = (uint32_t)e;
+            cp[q] = (int32_t)(e >> 32);
+            cval[q] = (int32_t)__hip_atomic_load(&x[kXVal + i], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
           }
         }
         // Every segment of the row has arrived, so none gave up: this one
@@ -2747,29 +2806,34 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
         if (t == 0)
           done_prev =
               __hip_atomic_fetch_add(&x[kXDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == 0) sm.word[6] = 0u;
-        __syncthreads();
-        const Cut cut = resolve_pairs_group<BS>(lcand, n, need, sm);
+        if (t == 0) sm.word[6] = 0u;  // published by the resolve's barriers
+        const Cut cut = resolve_pairs_regs<BS, kCandPer>(ck, cp, n, need, sm);
         // the segments' winners above the bin number h.before (the merged
-        // count): they took slots [0, h.before), the bin's take the rest
+        // count): they took slots [0, h.before), the bin's take the rest.
+        // One LDS atomic per wave takes the wave's slots.
         const uint32_t base = h.before;
+        uint64_t ms[kCandPer];
+        uint32_t wtot = 0;
 #pragma unroll
         for (int q = 0; q < kCandPer; ++q) {
-          const uint32_t i = (uint32_t)(q * BS + t);
-          const uint2 e = i < n ? lcand[i] : make_uint2(0u, 0u);
-          const bool s = (i < n) && is_selected(cut, e.x, (int32_t)e.y);
-          const uint64_t mm = __ballot(s);
-          if (mm == 0) continue;
-          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
-          const int leader = __builtin_ctzll(mm);
+          ms[q] = __ballot(is_selected(cut, ck[q], cp[q]));
+          wtot += (uint32_t)__builtin_popcountll(ms[q]);
+        }
+        if (wtot) {
           uint32_t wb = 0;
-          if (lane == leader) wb = atomicAdd(&sm.word[6], (uint32_t)__builtin_popcountll(mm));
-          wb = read_lane(wb, leader);
-          const uint32_t slot = wb + rank;
-          const int32_t j = (int32_t)e.y;
-          if (s & (slot < need) & ((uint32_t)j < (uint32_t)r.L) & (base + slot < k))
-            em.put((int32_t)(base + slot), j, cval[q]);
+          if (lane == 0) wb = atomicAdd(&sm.word[6], wtot);
+          wb = read_lane(wb, 0);
+#pragma unroll
+          for (int q = 0; q < kCandPer; ++q) {
+            const uint64_t mm = ms[q];
+            const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, wb));
+            const int32_t j = cp[q];
+            if (((mm >> lane) & 1ull) & (slot < need) & ((uint32_t)j < (uint32_t)r.L) &
+                (base + slot < k))
+              em.put((int32_t)(base + slot), j, cval[q]);
+            wb += (uint32_t)__builtin_popcountll(mm);
+          }
         }
         if (t == 0) sm.word[0] = done_prev == (uint32_t)S - 1u;
         __syncthreads();

@@ -229,10 +229,11 @@ def _plan_words(plan):
 # then per row its class-list entry, class, segment count and exchange
 # slot, then the long rows read whole (one word each), then 2 words per
 # work item (up to 33 per split row), then one
-# 8384-word exchange area per split row (histogram 0..4095, candidate pairs
-# 4096..8191, counters from 8192 on, each on a 128-byte line of its own).
+# 10432-word exchange area per split row (histogram 0..4095, candidate
+# pairs 4096..8191, their emitted values 8192..10239, counters from 10240
+# on, each on a 128-byte line of its own).
 MAX_SEG = 33
-X_WORDS = 8384
+X_WORDS = 10432
 
 
 def _layout(R):
@@ -268,10 +269,10 @@ def test_plan_reuse_and_exchange_reset(orc, name):
     assert words[17] == 0, "every long row of the batch is split"
     _, xarea = _layout(p.num_rows)
     x = words[xarea: xarea + n_split * X_WORDS].reshape(n_split, X_WORDS)
-    # histograms and counters must be zero again; the candidate pairs
-    # (words 4096..8191) are overwritten before they are read
+    # histograms and counters must be zero again; the candidate pairs and
+    # values (words 4096..10239) are overwritten before they are read
     assert not x[:, :4096].any(), "exchange histograms were not left zeroed"
-    assert not x[:, 8192:].any(), "exchange counters were not reset"
+    assert not x[:, 10240:].any(), "exchange counters were not reset"
 
 
 def test_split_row_that_gives_up_reads_minus_one(orc):
