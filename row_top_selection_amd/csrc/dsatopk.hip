@@ -89,6 +89,9 @@ struct Params {
   int32_t workers;
   // who reads the long rows that are not split (see LongMode)
   int32_t long_mode;
+  // register kernel with a plan: row workgroup g serves the plan's
+  // class-list entry num_rows - 1 - g (the longest classes first)
+  int32_t ordered;
 };
 
 // The long rows that are not split: with no plan, the streaming kernel
@@ -2974,7 +2977,20 @@ rows_reg_kernel(const Params p) {
     split_worker<kPaged>(p, sm.split);
     return;
   }
-  const int64_t b = (int64_t)blockIdx.x - p.workers;
+  int64_t b = (int64_t)blockIdx.x - p.workers;
+  if (p.ordered) {
+    // The plan lists the rows by class, shortest class first: read from the
+    // end, the longest rows start first and the last workgroups to be
+    // dispatched (after the split workers free their slots) serve short
+    // and trivial rows. A plan of another batch size leaves the order as
+    // it is.
+    const int32_t R = p.num_rows;
+    const int32_t pm = __builtin_amdgcn_readfirstlane(ld_const(p.plan + kPlanWordMagic));
+    const int32_t pr = __builtin_amdgcn_readfirstlane(ld_const(p.plan + kPlanWordRows));
+    const int32_t e = __builtin_amdgcn_readfirstlane(
+        ld_const(p.plan + kPlanHeaderWords + (R - 1 - (int32_t)b)));
+    if (pm == kPlanMagic && pr == R && (uint32_t)e < (uint32_t)R) b = e;
+  }
   const RowMeta m = row_meta<kPaged>(p, b, true);
   const RowInfo& r = m.r;
   // long rows: the split workers' or the streaming kernel's, unless the
@@ -3261,6 +3277,15 @@ constexpr int32_t kWideRows = 512;
 // whole) keeps the split path.
 constexpr int32_t kLongAllRows = 1024;
 
+// Up to this many rows, a register kernel launch with a plan serves the
+// rows in the plan's class order, longest first: in a small batch of
+// mixed lengths the rows that start last set the launch's end, and with
+// split rows those start only when the split workers free their slots
+// (512 rows of log-uniform lengths up to 131072: 27.2 -> 23.9 us). The
+// order costs each row one more scalar round trip; larger batches keep the
+// plain order.
+constexpr int32_t kOrderedRows = 1024;
+
 struct KernelLaunch {
   void (*fn)(Params);
   dim3 grid;
@@ -3282,6 +3307,7 @@ int launch_rows(Params p, hipStream_t stream) {
   const bool lng = p.stride > (int64_t)kBigCap;
   if (!lng) p.plan = nullptr;
   p.workers = 0;
+  p.ordered = 0;
   p.long_mode = !p.plan ? kLongPerRow
                         : (p.num_rows > kMaxSplitRows ? kLongListed : kLongInPieces);
   KernelLaunch ls[2];
@@ -3301,6 +3327,7 @@ int launch_rows(Params p, hipStream_t stream) {
     if (p.plan) {
       const int64_t w = plan_split_cap(p.num_rows) * kMaxSeg;
       p.workers = (int32_t)(w < kMaxWorkers ? w : kMaxWorkers);
+      p.ordered = p.num_rows <= kOrderedRows;
     }
     ls[n++] = {rows_reg_kernel<kPaged>, dim3((unsigned)(p.workers + p.num_rows)),
                dim3(kBigBlock)};
