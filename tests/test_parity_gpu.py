@@ -358,6 +358,26 @@ def test_stale_plan_gives_same_outputs(orc):
     assert dt.plan_error(plan) == 0
 
 
+def test_plan_of_a_larger_batch_gives_same_outputs(orc):
+    """A plan built for more rows (the batch's lengths followed by long
+    rows) is large enough for the call but belongs to another batch size:
+    the row kernels keep their own order and split nothing, and the
+    results stay exact."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    p = workloads.make_workload("paged_mixed")
+    d = gpu_run.to_dev(p)
+    more = np.concatenate([p.seq_lens, np.full(5, 131072, dtype=np.int32)])
+    plan = dt.plan(torch.from_numpy(more).to(d["lens"].device), p.k)
+    assert plan.numel() >= dt.plan_bytes(p.num_rows)
+    out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, plan=plan)
+    torch.cuda.synchronize()
+    assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), expected(orc, p),
+                      "larger plan")
+
+
 @pytest.mark.parametrize("page_size", [1, 2, 4096])
 def test_page_sizes(orc, page_size):
     rows = [(L, r, pat) for r in range(4) for L in (5000, 9000, 25000)
