@@ -97,9 +97,10 @@ size_t dsatopk_plan_bytes(int32_t num_rows);
  * with a zeroed exchange area per row through which the segments merge
  * their histograms. Longer rows of batches with more of them are read
  * whole by one workgroup each. Everything is computed on the device;
- * nothing is read back. The transform calls read only the split schedule:
- * rows of the other classes go to their kernel by their own length, with no
- * plan lookup before their data.
+ * nothing is read back. The transform calls read the split schedule, and
+ * in batches of up to 1024 rows at score strides above 40960 floats the
+ * class lists, whose order (longest class first) sets which rows start
+ * first; rows go to their kernel by their own length.
  *
  * The plan only schedules: a call given a plan built from different
  * seq_lens / row_starts / k, or no plan at all (NULL), returns the same
