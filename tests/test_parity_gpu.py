@@ -158,6 +158,58 @@ def test_band_edges(orc, band, k, mode):
     check(orc, p, use_plan=False, with_raw=(mode == "paged"))
 
 
+def _rank_bin_row(rng, L, above, cnt, dup):
+    """above keys at 5.0, then cnt keys inside one bin of the top 14 key
+    bits (floats just above 0.75, every dup-th one repeating its
+    predecessor: position ties inside the bin), the rest in (-1, 0.5)."""
+    v = rng.uniform(-1.0, 0.5, size=L).astype(np.float32)
+    idx = rng.permutation(L)[:above + cnt]
+    v[idx[:above]] = 5.0
+    bits = np.uint32(0x3F400001) + rng.permutation(1 << 16)[:cnt].astype(np.uint32)
+    if dup:
+        bits[dup::dup] = bits[dup - 1:-1:dup][:len(bits[dup::dup])]
+    v[idx[above:]] = bits.view(np.float32)
+    return v
+
+
+@pytest.mark.parametrize("mode", ["paged", "ragged"])
+@pytest.mark.parametrize("k", [2048, 1100])
+def test_decode_rank_bin_sizes(orc, mode, k):
+    """The decode rows' direct rank around its capacity: the k-th key's
+    14-bit bin holding 2, 64, 255, 256 (ranked) and 257, 400 (the 12-bit
+    fallback) elements, of which 1, half or all but one are taken, with and
+    without repeated keys, at every start residue (wide kernel: stride
+    8192, at most 512 rows)."""
+    from workloads.configs import OUTSIDE_SCORE, PAGE_SIZE, Problem, random_page_tables
+
+    rng = np.random.default_rng(7100 + k)
+    stride, L = 8192, 8000
+    rows = []
+    for cnt in (2, 64, 255, 256, 257, 400):
+        for take in sorted({1, cnt // 2, cnt - 1} - {0}):
+            for dup in (0, 3):
+                rows.append((cnt, take, dup))
+    R = len(rows) * 4
+    scores = np.full((R, stride), OUTSIDE_SCORE, dtype=np.float32)
+    starts = np.zeros(R, dtype=np.int32)
+    lens = np.full(R, L, dtype=np.int32)
+    for i, (cnt, take, dup) in enumerate(rows):
+        for r in range(4):
+            b = 4 * i + r
+            starts[b] = r + 4 * (b % 3)
+            scores[b, starts[b]:starts[b] + L] = _rank_bin_row(rng, L, k - take, cnt, dup)
+    assert R <= 512 and (starts + lens <= stride).all()
+    if mode == "ragged":
+        offs = rng.integers(0, 1 << 20, size=R).astype(np.int32)
+        p = Problem(f"rank_bins_{mode}_k{k}", "ragged", k, scores, lens, row_starts=starts,
+                    out_offsets=offs)
+    else:
+        pt = random_page_tables(rng, R, -(-L // PAGE_SIZE), 1 << 12)
+        p = Problem(f"rank_bins_{mode}_k{k}", "paged", k, scores, lens, row_starts=starts,
+                    page_table=pt, page_size=PAGE_SIZE)
+    check(orc, p, use_plan=False, with_raw=(mode == "paged"))
+
+
 def _long_all_rows(k, stride=65536):
     """Every start residue; lengths -3, 0, 1, k-1, k, k+1, 12000, the spans
     around 40960 and 49152 and the four spans below the stride; every value
