@@ -145,7 +145,7 @@ def _band_rows(k, stride):
 @pytest.mark.parametrize("band", list(BANDS))
 def test_band_edges(orc, band, k, mode):
     """The edge suite on the register kernels of short strides: the
-    1024-thread wide kernel (the paged decode kernel), the 256-thread short
+    512-thread wide kernel (the paged decode kernel), the 256-thread short
     kernel and both branches of the mid kernel, with trivial rows, every
     start residue, signed zeros, infinities, equal rows and tie classes."""
     stride, reps = BANDS[band]
