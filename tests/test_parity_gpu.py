@@ -108,7 +108,7 @@ def test_edge_batch(orc, mode, k, use_plan):
 
 
 # Score strides that select each register kernel (a row's span never exceeds
-# the stride): up to 8192 floats the short-row kernels (1024 threads per row
+# the stride): up to 8192 floats the short-row kernels (512 threads per row
 # up to 512 rows, 256 threads above), up to 16384 the mid kernel (8 or 16
 # float4 per thread by the row's span).
 BANDS = {
