@@ -483,13 +483,14 @@ def test_zero_rows_noop():
     assert out.shape == (0, 4)
 
 
-@pytest.mark.parametrize("name", ["paged_decode", "paged_long", "ragged_extend"])
+@pytest.mark.parametrize("name", ["paged_decode", "paged_long", "ragged_extend", "paged_mixed"])
 def test_graph_replay_matches_eager(orc, name):
     """plan + transform captured in a HIP graph: every replay, with eager
     work and synchronizations between replays, selects what the eager call
     and the oracle select (split rows included: their exchange areas must be
-    zero again for the next replay). Register-path rows are byte-equal; the
-    split path orders a row's outputs by segment arrival."""
+    zero again for the next replay; the mixed batch's register rows in the
+    plan's class order). Register-path rows are byte-equal; the split path
+    orders a row's outputs by segment arrival."""
     import torch
 
     import row_top_selection_amd as dt
