@@ -45,6 +45,12 @@ def _lib():
     if _handle is None:
         if not LIB_PATH.exists():
             raise ImportError(f"{LIB_PATH} is not built: run row_top_selection_amd.build.build()")
+        # torch's HIP runtime first: it carries the soname this library
+        # links against, so the library binds to it. Loaded the other way
+        # round, the process would hold a second HIP runtime, which knows
+        # none of torch's streams.
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(str(LIB_PATH))
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.dsatopk_status_string.argtypes = [ctypes.c_int]

@@ -691,3 +691,36 @@ def test_raw_positions_beside_paged(orc, name):
     sel = orc.select(p.scores, p.seq_lens, p.row_starts, p.k)
     assert_rows_equal(canonical(raw, p.seq_lens, p.k), sel, name + " raw")
     _check_raw_pairs(out, raw, p, None, None)
+
+
+def test_library_loaded_before_torch(orc, tmp_path):
+    """A process that asks for the library before it imports torch: the
+    binding loads torch's HIP runtime first, so the library binds to it and
+    takes torch's streams (with the library loaded first, the process held a
+    second HIP runtime that rejected them). A fresh interpreter, since the
+    load order is per process."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    dst = tmp_path / "out.npy"
+    code = "\n".join([
+        "import sys",
+        f"sys.path.insert(0, {root!r})",
+        "import numpy as np",
+        "import row_top_selection_amd as dt",
+        "dt.lib()",
+        "import torch",
+        "import workloads",
+        "p = workloads.make_workload('paged_small')",
+        "dev = torch.device('cuda:0')",
+        "out = dt.paged(torch.from_numpy(p.scores).to(dev), torch.from_numpy(p.seq_lens).to(dev),",
+        "               torch.from_numpy(p.page_table).to(dev), p.page_size, p.k)",
+        f"np.save({str(dst)!r}, out.cpu().numpy())",
+    ])
+    print("[gpu] library loaded before torch (subprocess)", flush=True)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=110)
+    assert res.returncode == 0, res.stderr[-2000:]
+    p = workloads.make_workload("paged_small")
+    assert_rows_equal(canonical(np.load(dst), p.seq_lens, p.k), expected(orc, p), p.name)
