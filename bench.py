@@ -11,7 +11,7 @@ reported beside it ("eager"), where host launch overhead dominates.
 
 Also reported (same JSON line):
   roofline      the paged transform kernel (rows_wide_kernel<true>: 128 short
-                rows, 1024 threads per row): algorithmic bytes per launch
+                rows, 512 threads per row): algorithmic bytes per launch
                 (scores of rows with L > k, outputs, page-table entries,
                 lengths) over its mean launch time from HIP events around a
                 graph of back-to-back launches.
@@ -19,7 +19,11 @@ Also reported (same JSON line):
                 scores per launch (L = 8192 ... 131072), timed in steady
                 state: after 0.1 s of untimed replays (the GPU's clocks ramp
                 up over the first ~10 ms of continuous work), the mean of 5
-                replays of 20 launches.
+                replays of 20 launches. Each carries "mover": the same
+                launch of bench_mover.hip, which reads the same windows and
+                writes the same k outputs per row with no selection, timed
+                the same way (what HBM allows for these bytes in this
+                launch shape; absent when bench_mover.so is not built).
   workloads     every named workload, one launch per iteration, cold, after
                 the same 0.1 s of untimed replays.
   cpu_baseline  the oracle on this host's cores over a bounded sample.
@@ -57,6 +61,49 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+MOVER_SRC = os.path.join(ROOT, "bench_mover.hip")
+MOVER_SO = os.path.join(ROOT, "bench_mover.so")
+
+
+def build_mover(verbose: bool = False) -> str:
+    """Compile bench_mover.hip (the same-bytes mover) for gfx950 beside it."""
+    import subprocess
+
+    from row_top_selection_amd import build as hip_build
+
+    tmp = MOVER_SO + ".tmp%d" % os.getpid()
+    cmd = [hip_build.HIPCC, "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", MOVER_SRC,
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, MOVER_SO)
+    return MOVER_SO
+
+
+_mover = None
+
+
+def mover_lib():
+    """The built same-bytes mover, or None when bench_mover.so is absent."""
+    global _mover
+    if _mover is None and os.path.exists(MOVER_SO):
+        import ctypes
+
+        import torch  # noqa: F401  (its HIP runtime first, as the library binding does)
+
+        lib = ctypes.CDLL(MOVER_SO)
+        lib.bench_mover.restype = ctypes.c_int
+        lib.bench_mover.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+        _mover = lib
+    return _mover
 
 
 def measured_traffic():
@@ -148,6 +195,18 @@ class Runner:
     def step(self, i: int):
         self.make_plan()
         self.transform(i)
+
+    def move(self, i: int):
+        """The same-bytes mover on copy i's scores (bench_mover.hip): the
+        window reads of rows with L > k and k int32 outputs per row."""
+        import torch
+
+        s = self.rot[i % self.copies]
+        rc = mover_lib().bench_mover(s.data_ptr(), s.stride(0), self.lens.data_ptr(),
+                                     self.p.num_rows, self.p.k, self.out.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"bench_mover failed ({rc})")
 
     def free(self):
         del self.rot, self.scores0
@@ -330,7 +389,8 @@ def only_workload(name: str):
     return workloads.make_workload(name)
 
 
-def measure_workload(p, iters: int, settle_s: float = SETTLE_S, reps: int = 1, **packed) -> dict:
+def measure_workload(p, iters: int, settle_s: float = SETTLE_S, reps: int = 1,
+                     mover: bool = False, **packed) -> dict:
     r = Runner(p, **packed)
     us = kernel_time_us(r.transform, iters, settle_s=settle_s, reps=reps)
     b = algorithmic_bytes(p)
@@ -339,8 +399,27 @@ def measure_workload(p, iters: int, settle_s: float = SETTLE_S, reps: int = 1, *
     res = dict(describe(p), transform_us=us, rows_per_s=p.num_rows / (us * 1e-6),
                score_GBps=b["score"] / (us * 1e3), total_GBps=b["total"] / (us * 1e3),
                hbm_frac=b["total"] / (us * 1e3) / HBM_PEAK_GBPS, bytes=b, rotation=r.copies)
+    if mover and mover_lib() is not None and not packed:
+        # the same reads and writes with no selection, timed the same way
+        mus = kernel_time_us(r.move, iters, settle_s=settle_s, reps=reps)
+        res["mover"] = {"us": mus, "score_frac": b["score"] / (mus * 1e3) / HBM_PEAK_GBPS,
+                        "transform_over_mover": us / mus}
     r.free()
     return res
+
+
+def measure_sustained() -> dict:
+    import torch
+
+    sus = {}
+    for name, mk in sustained_makers().items():
+        # steady state: 0.1 s of untimed replays, then 5 x 20 launches
+        res = measure_workload(mk(), 20, reps=5, mover=True)
+        res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
+        res["timing"] = f"mean of 5 replays of 20 launches after {SETTLE_S} s of replays"
+        sus[name] = res
+        torch.cuda.empty_cache()
+    return sus
 
 
 def main(argv=None):
@@ -355,6 +434,8 @@ def main(argv=None):
     ap.add_argument("--only", default=None,
                     help="only replay one workload's transform --steps times (counter runs): "
                          "a workload name, a sustained name, or all_trivial")
+    ap.add_argument("--sustained-only", action="store_true",
+                    help="only the sustained launches (and their mover), as one JSON line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the selection shards by rows with no exchange, "
@@ -374,6 +455,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_CALIBRATION_BYTES, "launches": 5}), flush=True)
         return 0
+    if args.sustained_only:
+        print(json.dumps({"sustained": measure_sustained(),
+                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return 0
     if args.only:
         p = only_workload(args.only)
         r = Runner(p)
@@ -391,6 +476,7 @@ def main(argv=None):
     b = algorithmic_bytes(p)
     k_us = kernel_time_us(r.transform, max(args.steps, 50))
     plan_us = kernel_time_us(lambda i: r.make_plan(), 50)
+    mover_us = kernel_time_us(r.move, max(args.steps, 50)) if mover_lib() is not None else None
     achieved = b["total"] / (k_us * 1e3)
     line = {
         "metric": METRIC,
@@ -420,7 +506,7 @@ def main(argv=None):
                      "kernel": "dsatopk::rows_wide_kernel<true>", "kernel_us": k_us,
                      "kernel_source_hash": kernel_source_hash(),
                      "bytes_per_launch": b, "score_GBps": b["score"] / (k_us * 1e3),
-                     "plan_us": plan_us},
+                     "plan_us": plan_us, "mover_us": mover_us},
     }
     r.free()
     del r
@@ -428,15 +514,7 @@ def main(argv=None):
     if not args.quick:
         # paged decode rows from 8192 to 131072 columns, 1 GiB of scores per
         # launch (the decode and long-context shapes, and three between)
-        sus = {}
-        for name, mk in sustained_makers().items():
-            # steady state: 0.1 s of untimed replays, then 5 x 20 launches
-            res = measure_workload(mk(), 20, reps=5)
-            res["score_frac"] = res["score_GBps"] / HBM_PEAK_GBPS
-            res["timing"] = f"mean of 5 replays of 20 launches after {SETTLE_S} s of replays"
-            sus[name] = res
-            torch.cuda.empty_cache()
-        line["sustained"] = sus
+        line["sustained"] = measure_sustained()
         wl = {}
         for name in workloads.WORKLOADS:
             wl[name] = measure_workload(workloads.make_workload(name), 50)
