@@ -18,15 +18,18 @@
 //     later pass runs over those. 512 threads per row for small batches of
 //     short strides, 256 threads up to a 16384 stride, 512 threads up to
 //     40960-float spans for longer strides, and 1024-thread workgroups of
-//     the long-row kernel up to 65536 (for a batch of 1024 rows or more
-//     whose stride is at most 65536, every row of it);
+//     the long-row kernel up to 65536 (without a plan; with one, for a
+//     batch of 1024 rows or more whose stride is at most 57344, every row
+//     of it);
 //   - long rows of batches with few of them (split rows): cut into
 //     segments of 4096 or 8192 floats, each held in registers by one
 //     workgroup of the register kernel; the segments merge their digit
 //     histograms through an exchange area in the plan buffer;
-//   - the other long rows (span above 65536): streamed once by a
-//     1024-thread workgroup that keeps the pairs above a running threshold
-//     in LDS (a two-pass re-read serves the rare rows that defeat it).
+//   - the other long rows: with a plan, read in pieces of 16384 floats by
+//     a 512-thread workgroup of the register kernel; without one, streamed
+//     by a 1024-thread workgroup above 65536. Both keep the pairs above a
+//     running threshold in LDS (a two-pass re-read serves the rare rows
+//     that defeat it).
 // The pages' CUDA design (register rows up to 8192 / 16384, a streaming
 // template, thread-block clusters for very long rows; PR #26788 and
 // PR #36684 digests) is prior art here: the widths and the capacities are
@@ -94,17 +97,14 @@ struct Params {
   int32_t ordered;
 };
 
-// The long rows that are not split: with no plan, the streaming kernel
-// (one workgroup per row of the batch); with a plan of a batch of more than
-// kMaxSplitRows rows, the streaming kernel serves the plan's streamed list
-// (workgroup g its entry g) and the register kernel, in pieces, any long
-// row the plan does not list (a plan built for other lengths); with a plan
-// of a smaller batch (every long row split), the register kernel, in
-// pieces, any long row the plan does not split. kLongAll: a large batch
-// whose stride keeps every row in 1024 threads' registers (see
-// launch_rows): the long-row kernel alone serves every row, one
-// workgroup per row, and no row is split.
-enum LongMode : int32_t { kLongPerRow = 0, kLongListed = 1, kLongInPieces = 2, kLongAll = 3 };
+// The long rows that are not split: with no plan, the long-row kernel
+// (one 1024-thread workgroup per row of the batch); with a plan, the
+// register kernel, in pieces (three rows per CU), and the long-row kernel
+// is not launched. kLongAll: a large batch whose stride keeps every row in
+// 1024 threads' registers and is at most kLongAllStride (see launch_rows):
+// the long-row kernel alone serves every row, one workgroup per row, and
+// no row is split.
+enum LongMode : int32_t { kLongPerRow = 0, kLongInPieces = 1, kLongAll = 2 };
 
 // Row classes by aligned span. A row's class is recomputed by every kernel
 // from the current seq_lens / row_starts; the plan only packs the rows of a
@@ -114,9 +114,8 @@ constexpr int kNumClasses = 4;
 
 // Plan layout (int32 words): a 64-word header; the rows of each class
 // (class order); each row's class, segment count and exchange slot; the
-// long rows read whole (their own array, at a fixed place, so that a
-// workgroup loads its entry with the header); the (row, segment) work items
-// of split rows; one exchange area per split row.
+// (row, segment) work items of split rows; one exchange area per split
+// row.
 constexpr int kPlanMagic = 0x44534b33;  // "DSK3"
 constexpr int kPlanHeaderWords = 64;
 enum PlanWord : int32_t {
@@ -130,7 +129,6 @@ enum PlanWord : int32_t {
   kPlanWordError = 14,       // set when a split segment gave up waiting for its row
   kPlanWordSpin = 15,        // polls before such a wait gives up (0: kSpinLimit)
   kPlanWordSegLen = 16,      // floats per segment of the split rows
-  kPlanWordStreamed = 17,    // long rows read whole by the streaming kernel (class-list order)
 };
 
 // Long rows are cut into segments of 4096 or 8192 aligned floats, one
@@ -181,8 +179,7 @@ __host__ __device__ constexpr int64_t plan_split_cap(int64_t rows) {
 __host__ __device__ constexpr int64_t plan_cls_word(int64_t rows) { return kPlanHeaderWords + rows; }
 __host__ __device__ constexpr int64_t plan_nseg_word(int64_t rows) { return kPlanHeaderWords + 2 * rows; }
 __host__ __device__ constexpr int64_t plan_slot_word(int64_t rows) { return kPlanHeaderWords + 3 * rows; }
-__host__ __device__ constexpr int64_t plan_stream_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
-__host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 5 * rows; }
+__host__ __device__ constexpr int64_t plan_items_word(int64_t rows) { return kPlanHeaderWords + 4 * rows; }
 __host__ __device__ constexpr int64_t plan_xarea_word(int64_t rows) {
   return (plan_items_word(rows) + 2 * plan_split_cap(rows) * kMaxSeg + 63) / 64 * 64;
 }
@@ -2078,7 +2075,6 @@ struct RowMeta {
   int32_t slot;     // plan: the row's exchange area (split rows)
   int32_t seg_len;  // plan: floats per segment
   bool split;       // the plan sends the row to the split workers
-  bool streamed;    // the plan lists the row as a long row read whole
 };
 
 template <bool kPaged>
@@ -2094,17 +2090,15 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   const int32_t* a_pg = hp ? p.plan + kPlanWordSegLen : a_len;
   const int32_t* a_ps = hp ? p.plan + plan_nseg_word(p.num_rows) + b : a_len;
   const int32_t* a_pl = hp ? p.plan + plan_slot_word(p.num_rows) + b : a_len;
-  const int32_t* a_pc = hp ? p.plan + plan_cls_word(p.num_rows) + b : a_len;
   // (readfirstlane: a no-op on scalar loads; a vector load, where the
   // compiler cannot prove the words unchanged, still ends in an SGPR)
   auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(ld_const(a)); };
   int32_t len = rd(a_len), rs = rd(a_rs), tr = rd(a_tr), ts = rd(a_ts), of = rd(a_of);
-  int32_t pm = rd(a_pm), pr = rd(a_pr), pg = rd(a_pg), ps = rd(a_ps), pl = rd(a_pl),
-          pc = rd(a_pc);
+  int32_t pm = rd(a_pm), pr = rd(a_pr), pg = rd(a_pg), ps = rd(a_ps), pl = rd(a_pl);
   // every value is needed here: the compiler may not sink a load into the
   // branch that uses it (which would put it behind another load's wait)
   asm volatile("" : "+s"(len), "+s"(rs), "+s"(tr), "+s"(ts), "+s"(of), "+s"(pm), "+s"(pr),
-               "+s"(pg), "+s"(ps), "+s"(pl), "+s"(pc));
+               "+s"(pg), "+s"(ps), "+s"(pl));
   RowMeta m;
   RowInfo& r = m.r;
   r = classify(len, p.row_starts ? rs : 0, p.k);
@@ -2121,7 +2115,6 @@ __device__ __forceinline__ RowMeta row_meta(const Params& p, int64_t b, bool wit
   const bool ours = hp && pm == kPlanMagic && pr == p.num_rows;
   m.split = ours && r.cls == kClassLong && (pg == kSegShort || pg == kSegLong) && ps >= 2 &&
             ps == segments_for(r.span, pg) && pl >= 0 && pl < plan_split_cap(p.num_rows);
-  m.streamed = ours && pc == kClassLong && ps == 0;
   return m;
 }
 
@@ -2720,7 +2713,6 @@ __device__ __forceinline__ void split_segment(const Params& p, int64_t b, const 
   const RowInfo& r = m.r;
   const int32_t t = tix();
   const int lane = lane_id();
-  const int w = wave_id();
   const uint32_t k = (uint32_t)p.k;
   const int32_t S = m.nseg;
   const SplitSync sy{x, S, p.plan + kPlanWordError, spin, sm.word};
@@ -2993,11 +2985,8 @@ rows_reg_kernel(const Params p) {
   }
   const RowMeta m = row_meta<kPaged>(p, b, true);
   const RowInfo& r = m.r;
-  // long rows: the split workers' or the streaming kernel's, unless the
-  // plan leaves them to this kernel
-  if (r.cls == kClassLong &&
-      (m.split || p.long_mode == kLongPerRow || (p.long_mode == kLongListed && m.streamed)))
-    return;
+  // long rows: the split workers', or without a plan the long-row kernel's
+  if (r.cls == kClassLong && (m.split || p.long_mode == kLongPerRow)) return;
   const Emit<kPaged> em = row_emit<kPaged>(p, b, m);
   if (r.L <= p.k) {
     write_trivial<kPaged, kBigBlock>(em, r.L, p.k);
@@ -3026,11 +3015,10 @@ constexpr int kLongRegVec = 13;
 constexpr int kLongLds = 3;
 constexpr int kLongRegCap = (kLongRegVec + kLongLds) * 4 * kLongBlock;  // 65536
 
-// Long rows read whole, one 1024-thread workgroup at a time: with no plan
-// one workgroup per row of the batch (the others leave at once); with a
-// plan a persistent grid, workgroup g reading the plan's streamed rows g,
-// g + G, ... (G workgroups), each row during its final cut touching the
-// opening lines of the row it reads next.
+// Long rows read whole, one 1024-thread workgroup per row of the batch
+// (the workgroups of other rows leave at once): from registers up to 65536
+// floats, else streamed, each streamed row touching during its final cut
+// the opening lines of the row likely to start next.
 template <bool kPaged>
 __device__ __forceinline__ void long_row(const Params& p, int64_t b, const RowMeta& m,
                                          const Prefetch pf) {
@@ -3056,47 +3044,28 @@ __device__ __forceinline__ void long_row(const Params& p, int64_t b, const RowMe
 template <bool kPaged>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(8))) void
 rows_long_kernel(const Params p) {
-  // Workgroup g reads row g of the batch, or with a plan entry g of the
-  // plan's streamed rows. (A persistent grid looping over the list would
-  // launch fewer workgroups, but the loop keeps values the compiler hoists
-  // out of it live through the row's body, which spills at the 64 VGPRs of
-  // two workgroups per CU.) Every word read before the scores comes in two
-  // round trips: the plan's header words with this workgroup's and the
-  // touched row's entries, then both rows' words.
-  const int32_t g = blockIdx.x;
+  // Workgroup g reads row g of the batch; the launch takes no plan. (A
+  // persistent grid would launch fewer workgroups, but its loop keeps
+  // values the compiler hoists out of it live through the row's body,
+  // which spills at the 64 VGPRs of two workgroups per CU.)
+  const int64_t b = blockIdx.x;
+  const int64_t b2 = b + kPrefetchAhead;  // the row likely to start next on this XCD
   const int32_t R = p.num_rows;
-  int64_t b = g;
-  int64_t b2 = g + kPrefetchAhead;  // the row likely to start next on this XCD
-  if (p.long_mode == kLongListed) {
-    const int32_t* st = p.plan + plan_stream_word(R);
-    const int32_t* a_n = p.plan + kPlanWordStreamed;
-    const int32_t* a_b = st + g;
-    const int32_t* a_b2 = g + kPrefetchAhead < R ? st + g + kPrefetchAhead : a_n;
-    auto rd = [](const int32_t* a) { return __builtin_amdgcn_readfirstlane(ld_const(a)); };
-    int32_t pm = rd(p.plan + kPlanWordMagic), pr = rd(p.plan + kPlanWordRows), n = rd(a_n),
-            e = rd(a_b), e2 = rd(a_b2);
-    asm volatile("" : "+s"(pm), "+s"(pr), "+s"(n), "+s"(e), "+s"(e2));
-    if (pm != kPlanMagic || pr != R || g >= n || n > R) return;
-    b = e;
-    b2 = g + kPrefetchAhead < n ? e2 : -1;
-    if ((uint64_t)b >= (uint64_t)R) return;
-  }
   // the touched row's words, loaded with the row's own
   const bool t2 = (uint64_t)b2 < (uint64_t)R;
   const int32_t* a_l2 = t2 ? p.seq_lens + b2 : p.seq_lens + b;
   const int32_t* a_s2 = (t2 && p.row_starts) ? p.row_starts + b2 : a_l2;
   int32_t l2 = __builtin_amdgcn_readfirstlane(ld_const(a_l2));
   int32_t s2 = __builtin_amdgcn_readfirstlane(ld_const(a_s2));
-  const RowMeta m = row_meta<kPaged>(p, b, true);
+  const RowMeta m = row_meta<kPaged>(p, b, false);
   asm volatile("" : "+s"(l2), "+s"(s2));
   if (p.long_mode == kLongAll) {
     if (m.r.L <= p.k) {
       write_trivial<kPaged, kLongBlock>(row_emit<kPaged>(p, b, m), m.r.L, p.k);
       return;
     }
-  } else {
-    if (m.r.cls != kClassLong || m.split) return;
-    if (p.long_mode == kLongListed && !m.streamed) return;
+  } else if (m.r.cls != kClassLong) {
+    return;
   }
   Prefetch pf{nullptr, 0};
   if (t2) {
@@ -3204,12 +3173,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
 #pragma unroll
   for (int c = 1; c < kNumClasses; ++c) off[c] = off[c - 1] + count[c - 1];
   int32_t* list = plan + kPlanHeaderWords;
-  int32_t* stream = plan + plan_stream_word(num_rows);
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const int32_t c = cls[b];
     const uint32_t at = atomicAdd(&fill[c], 1u);
     list[off[c] + at] = b;
-    if (c == kClassLong && !split) stream[at] = b;
   }
   if (tix() == 0) {
     plan[kPlanWordMagic] = kPlanMagic;
@@ -3224,7 +3191,6 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     plan[kPlanWordError] = 0;
     plan[kPlanWordSpin] = 0;
     plan[kPlanWordSegLen] = seg_len;
-    plan[kPlanWordStreamed] = split ? 0 : (int32_t)count[kClassLong];
   }
 }
 
@@ -3276,6 +3242,13 @@ constexpr int32_t kWideRows = 512;
 // (few long rows among many short ones: 300 rows at 20 us split, 29 us
 // whole) keeps the split path.
 constexpr int32_t kLongAllRows = 1024;
+// ... and, with a plan, for strides up to this. Longer rows hold more of
+// their span in the long kernel's LDS slices and cut and stage over more
+// keys: from 61440 columns the register kernel's pieces (three rows per
+// CU) take less time (rows of 57344 / 61440 / 65536 floats, 1 GiB of
+// scores per launch: 213 / 217 / 220 us in the long kernel, 219 / 212 /
+// 208 us in pieces; at 49152, 214 against 219).
+constexpr int64_t kLongAllStride = 57344;
 
 // Up to this many rows, a register kernel launch with a plan serves the
 // rows in the plan's class order, longest first: in a small batch of
@@ -3296,11 +3269,14 @@ struct KernelLaunch {
 // row's span never exceeds it). Up to 8192 floats every row is short: the
 // short-row kernel (or the wide one, for few rows) serves the batch alone;
 // up to 16384 the mid kernel alone; up to 40960 the register kernel alone;
-// up to 65536, from kLongAllRows rows, the long-row kernel alone (the plan
-// is not used). Other strides: the register kernel, whose first
-// workgroups are the split workers when a plan is given, then the
-// streaming kernel, unless the plan splits every long row (at most
-// kMaxSplitRows rows). Each launch reports its own status.
+// from kLongAllRows rows, up to kLongAllStride (without a plan, up to
+// 65536) the long-row kernel alone (the plan is not used). Other strides: the register kernel, whose first
+// workgroups are the split workers when a plan is given and which then
+// also reads the long rows that are not split, in pieces; without a plan
+// the long-row kernel follows it for the long rows (many long rows of
+// 98304 or 131072 floats, 1 GiB per launch: 215 / 211 us with the
+// long-row kernel's 1024-thread streamed rows, 199 / 198 us in pieces).
+// Each launch reports its own status.
 template <bool kPaged>
 int launch_rows(Params p, hipStream_t stream) {
   const dim3 grid((unsigned)p.num_rows);
@@ -3308,8 +3284,7 @@ int launch_rows(Params p, hipStream_t stream) {
   if (!lng) p.plan = nullptr;
   p.workers = 0;
   p.ordered = 0;
-  p.long_mode = !p.plan ? kLongPerRow
-                        : (p.num_rows > kMaxSplitRows ? kLongListed : kLongInPieces);
+  p.long_mode = p.plan ? kLongInPieces : kLongPerRow;
   KernelLaunch ls[2];
   int n = 0;
   if (p.stride <= (int64_t)kSmallVec * 4 * kBlock) {
@@ -3319,7 +3294,8 @@ int launch_rows(Params p, hipStream_t stream) {
       ls[n++] = {rows_short_kernel<kPaged>, grid, dim3(kBlock)};
   } else if (p.stride <= (int64_t)kLargeVec * 4 * kBlock) {
     ls[n++] = {rows_mid_kernel<kPaged>, grid, dim3(kBlock)};
-  } else if (lng && p.stride <= (int64_t)kLongRegCap && p.num_rows >= kLongAllRows) {
+  } else if (lng && p.num_rows >= kLongAllRows &&
+             p.stride <= (p.plan ? kLongAllStride : (int64_t)kLongRegCap)) {
     p.plan = nullptr;
     p.long_mode = kLongAll;
     ls[n++] = {rows_long_kernel<kPaged>, grid, dim3(kLongBlock)};
