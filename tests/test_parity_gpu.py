@@ -230,17 +230,22 @@ def _long_all_rows(k, stride=65536):
     return rows
 
 
-@pytest.mark.parametrize("mode,k,use_plan", [("paged", 2048, True), ("paged", 7, False),
-                                             ("ragged", 2048, False), ("ragged", 1, True)])
-def test_long_kernel_serves_every_row(orc, mode, k, use_plan):
-    """A batch of 1024 rows or more at a score stride of 65536 floats: the
-    long-row kernel alone serves every row (trivial, short, register-length
-    and long, up to the stride), with every start residue, the value
-    patterns and tie classes; a plan, when given, is not used."""
-    rows = _long_all_rows(k)
+@pytest.mark.parametrize("mode,k,use_plan,stride", [
+    ("paged", 2048, True, 57344), ("ragged", 1, True, 57344),
+    ("paged", 7, False, 65536), ("ragged", 2048, False, 65536),
+    ("paged", 2048, True, 65536), ("ragged", 1, True, 65536)])
+def test_large_batch_at_long_strides(orc, mode, k, use_plan, stride):
+    """A batch of 1024 rows or more at a score stride of 57344 or 65536
+    floats, with every row kind (trivial, short, register-length and long,
+    up to the stride), every start residue, the value patterns and tie
+    classes. Up to 57344 (65536 without a plan) the long-row kernel alone
+    serves every row and a given plan is not used; at 65536 with a plan
+    the register kernel serves them, the long rows in pieces."""
+    rows = _long_all_rows(k, stride)
     rows = rows * (1024 // len(rows) + 1)
-    p = edge_batch(6000 + k, mode, k, rows, stride=65536, name=f"long_all_{mode}_k{k}")
-    assert p.stride == 65536 and p.num_rows >= 1024
+    p = edge_batch(6000 + k + stride, mode, k, rows, stride=stride,
+                   name=f"long_all_{mode}_k{k}_s{stride}")
+    assert p.stride == stride and p.num_rows >= 1024
     check(orc, p, use_plan=use_plan, with_raw=(mode == "paged"))
 
 
