@@ -100,8 +100,8 @@ def mover_lib():
         lib = ctypes.CDLL(MOVER_SO)
         lib.bench_mover.restype = ctypes.c_int
         lib.bench_mover.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                    ctypes.c_void_p]
+                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
         _mover = lib
     return _mover
 
@@ -202,7 +202,8 @@ class Runner:
         import torch
 
         s = self.rot[i % self.copies]
-        rc = mover_lib().bench_mover(s.data_ptr(), s.stride(0), self.lens.data_ptr(),
+        starts = None if self.starts is None else self.starts.data_ptr()
+        rc = mover_lib().bench_mover(s.data_ptr(), s.stride(0), self.lens.data_ptr(), starts,
                                      self.p.num_rows, self.p.k, self.out.data_ptr(),
                                      torch.cuda.current_stream().cuda_stream)
         if rc != 0:
@@ -517,7 +518,7 @@ def main(argv=None):
         line["sustained"] = measure_sustained()
         wl = {}
         for name in workloads.WORKLOADS:
-            wl[name] = measure_workload(workloads.make_workload(name), 50)
+            wl[name] = measure_workload(workloads.make_workload(name), 50, mover=True)
             torch.cuda.empty_cache()
         line["workloads"] = wl
         # the packed PAGED layout (4 requests x 1024 query rows sharing their
