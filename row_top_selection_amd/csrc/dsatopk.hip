@@ -3139,9 +3139,15 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   int32_t* slot = plan + plan_slot_word(num_rows);
   int32_t* items = plan + plan_items_word(num_rows);
   const uint32_t cap = (uint32_t)plan_split_cap(num_rows);
+  // With one row per thread, each thread keeps its row's class in a
+  // register for the later passes; otherwise they read it back from the
+  // plan (a round trip to L2 after each barrier).
+  const bool one_each = num_rows <= kPlanBlock;
+  int32_t my_cls = -1;
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     const RowInfo r = row_info(seq_lens, row_starts, k, b);
     cls[b] = r.cls;
+    my_cls = r.cls;
     atomicAdd(&count[r.cls], 1u);
     if (r.cls == kClassLong) atomicAdd(&n_seg_long, (uint32_t)segments_for(r.span, kSegLong));
   }
@@ -3153,7 +3159,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
     int32_t S = 0;
     int32_t q = -1;
-    if (split && cls[b] == kClassLong) {
+    if (split && (one_each ? my_cls : cls[b]) == kClassLong) {
       const RowInfo r = row_info(seq_lens, row_starts, k, b);
       S = segments_for(r.span, seg_len);
       q = (int32_t)atomicAdd(&n_split, 1u);
@@ -3174,7 +3180,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   for (int c = 1; c < kNumClasses; ++c) off[c] = off[c - 1] + count[c - 1];
   int32_t* list = plan + kPlanHeaderWords;
   for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
-    const int32_t c = cls[b];
+    const int32_t c = one_each ? my_cls : cls[b];
     const uint32_t at = atomicAdd(&fill[c], 1u);
     list[off[c] + at] = b;
   }
