@@ -3080,7 +3080,11 @@ rows_long_kernel(const Params p) {
 }
 
 // Plan: classify every row and list the rows of each class (workgroup 0).
+// Workgroups of up to this many threads: a batch of at most that many rows
+// takes the least multiple of 64 threads that covers its rows, and at least
+// kPlanMinBlock (the exchange areas' zeroing keeps enough threads).
 constexpr int kPlanBlock = 1024;
+constexpr int kPlanMinBlock = 256;
 
 // Up to this many rows the plan is one launch: its workgroups after the
 // first zero the exchange areas, each counting the batch's long rows by
@@ -3116,7 +3120,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
     const int64_t cap = plan_split_cap(num_rows);
     const int32_t q = (int32_t)blockIdx.x - 1;
     if ((int64_t)n_long <= cap && (int64_t)q < (int64_t)n_long)
-      zero_area(num_rows, plan, q, kPlanBlock);
+      zero_area(num_rows, plan, q, (int32_t)blockDim.x);
     return;
   }
   __shared__ uint32_t count[kNumClasses];
@@ -3142,9 +3146,10 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   // With one row per thread, each thread keeps its row's class in a
   // register for the later passes; otherwise they read it back from the
   // plan (a round trip to L2 after each barrier).
-  const bool one_each = num_rows <= kPlanBlock;
+  const int32_t nb = (int32_t)blockDim.x;
+  const bool one_each = num_rows <= nb;
   int32_t my_cls = -1;
-  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
+  for (int32_t b = tix(); b < num_rows; b += nb) {
     const RowInfo r = row_info(seq_lens, row_starts, k, b);
     cls[b] = r.cls;
     my_cls = r.cls;
@@ -3156,7 +3161,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
   // segments when long ones would leave CUs idle
   const bool split = count[kClassLong] <= cap;
   const int32_t seg_len = n_seg_long < (uint32_t)kChipCUs ? kSegShort : kSegLong;
-  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
+  for (int32_t b = tix(); b < num_rows; b += nb) {
     int32_t S = 0;
     int32_t q = -1;
     if (split && (one_each ? my_cls : cls[b]) == kClassLong) {
@@ -3179,7 +3184,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_kernel(const int32_t* seq_len
 #pragma unroll
   for (int c = 1; c < kNumClasses; ++c) off[c] = off[c - 1] + count[c - 1];
   int32_t* list = plan + kPlanHeaderWords;
-  for (int32_t b = tix(); b < num_rows; b += kPlanBlock) {
+  for (int32_t b = tix(); b < num_rows; b += nb) {
     const int32_t c = one_each ? my_cls : cls[b];
     const uint32_t at = atomicAdd(&fill[c], 1u);
     list[off[c] + at] = b;
@@ -3383,11 +3388,14 @@ int dsatopk_plan(const int32_t* seq_lens, const int32_t* row_starts, int32_t num
   if ((reinterpret_cast<uintptr_t>(plan) & 15u) != 0) return DSATOPK_ERR_ALIGNMENT;
   const int64_t cap = plan_split_cap(num_rows);
   const bool fused = num_rows <= kFusedClearRows;
+  // a fused launch's counting workgroups need a thread per row
+  const int32_t cover = (num_rows + 63) / 64 * 64;
+  const int32_t pb = !fused ? kPlanBlock : (cover < kPlanMinBlock ? kPlanMinBlock : cover);
   int32_t* pl = static_cast<int32_t*>(plan);
   {
     void* args[] = {&seq_lens, &row_starts, &num_rows, &k, &pl};
     if (hipLaunchKernel(reinterpret_cast<const void*>(plan_kernel),
-                        dim3(fused ? (unsigned)(1 + cap) : 1u), dim3(kPlanBlock), args, 0,
+                        dim3(fused ? (unsigned)(1 + cap) : 1u), dim3((unsigned)pb), args, 0,
                         (hipStream_t)stream) != hipSuccess)
       return DSATOPK_ERR_HIP;
   }
