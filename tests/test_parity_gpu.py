@@ -281,11 +281,10 @@ def _plan_words(plan):
 
 
 # The plan's layout (int32 words), as the library writes it: a 64-word
-# header (word 12 the split rows, 13 their work items, 14 the error word,
-# 15 the poll limit, 16 the segment length, 17 the long rows read whole),
-# then per row its class-list entry, class, segment count and exchange
-# slot, then the long rows read whole (one word each), then 2 words per
-# work item (up to 33 per split row), then one
+# header (words 4..7 the rows per class, 12 the split rows, 13 their work
+# items, 14 the error word, 15 the poll limit, 16 the segment length), then
+# per row its class-list entry, class, segment count and exchange slot,
+# then 2 words per work item (up to 33 per split row), then one
 # 10432-word exchange area per split row (histogram 0..4095, candidate
 # pairs 4096..8191, their emitted values 8192..10239, counters from 10240
 # on, each on a 128-byte line of its own).
@@ -329,6 +328,42 @@ def test_plan_reuse_and_exchange_reset(orc, name):
     # values (words 4096..10239) are overwritten before they are read
     assert not x[:, :4096].any(), "exchange histograms were not left zeroed"
     assert not x[:, 10240:].any(), "exchange counters were not reset"
+
+
+@pytest.mark.parametrize("R", [1, 65, 300, 1000])
+def test_plan_of_any_batch_size_splits_and_zeroes(orc, R):
+    """Plans whose workgroups take 256, 320 and 1024 threads (the least
+    multiple of 64 covering the rows, at least 256), each over a batch of
+    trivial rows with long rows at its first, middle and last positions:
+    the plan splits every long row and zeroes each split row's exchange
+    area in a buffer that starts out full of garbage, and the transform
+    with it equals the oracle."""
+    import torch
+
+    import row_top_selection_amd as dt
+
+    long_at = sorted({0, R // 2, R - 1})
+    rows = [(100, 0, "normal")] * R
+    for i in long_at:
+        rows[i] = (70000 - i % 4, i % 4, "normal")
+    p = edge_batch(7100 + R, "paged", 2048, rows, name=f"plan_block_{R}")
+    print(f"[gpu] plan block R={R}", flush=True)
+    d = gpu_run.to_dev(p)
+    plan = torch.full((dt.plan_bytes(R),), 0x5A, dtype=torch.uint8, device=d["lens"].device)
+    dt.plan(d["lens"], p.k, row_starts=d["starts"], out=plan)
+    torch.cuda.synchronize()
+    words = _plan_words(plan)
+    n_split = int(words[12])
+    assert words[4 + 3] == len(long_at) and n_split == len(long_at)
+    _, xarea = _layout(R)
+    x = words[xarea: xarea + n_split * X_WORDS].reshape(n_split, X_WORDS)
+    assert not x[:, :4096].any(), "exchange histograms were not zeroed"
+    assert not x[:, 10240:].any(), "exchange counters were not zeroed"
+    out = dt.paged(d["scores"], d["lens"], d["pt"], p.page_size, p.k, row_starts=d["starts"],
+                   plan=plan)
+    torch.cuda.synchronize()
+    assert_rows_equal(canonical(out.cpu().numpy(), p.seq_lens, p.k), expected(orc, p), p.name)
+    assert dt.plan_error(plan) == 0
 
 
 def test_split_row_that_gives_up_reads_minus_one(orc):
